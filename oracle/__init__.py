@@ -1,0 +1,8 @@
+"""CPU oracle (float64, NumPy) of the multi-scale deformable attention sampling core.
+
+TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
+benchmark's CPU-baseline leg, never by the library or its binding. It shares no
+code with the HIP path.
+"""
+from .msda_oracle import (msda_backward, msda_forward, msda_grad_value_rows,  # noqa: F401
+                          pixel_coordinate)

@@ -1,0 +1,239 @@
+"""fp64 CPU oracle of the multi-scale deformable attention sampling core.
+
+TEST INFRASTRUCTURE. Only the tests, the smoke check and the CPU-baseline leg of
+the benchmark may import or run this module. The HIP library and its Python
+binding never call it, and it imports nothing from them.
+
+What is computed (page "Deformable DETR", section "Multi-scale deformable
+attention", equation MSDeformAttn, restricted to the part inside the outer
+projection W_m and with W'_m already applied to the value map): for every batch
+image n, query q and head m,
+
+    out[n,q,m,:] = sum_l sum_k A[n,q,m,l,k] * x^l_m( phi_l(p_hat_q) + dp[n,q,m,l,k] )
+
+where x^l_m(.) reads level l of head m's value map at a fractional location by
+bilinear interpolation of the four surrounding pixels (same page, section
+"Deformable attention module", symbol list; page "Deformable Attention Module",
+"bilinear interpolation is applied as in Dai et al. (2017)"; page "Deformable
+Attention", bilinear from the four nearest pixels). The library receives the
+sampling location already formed, as normalised coordinates
+loc = phi_l-normalised reference + offset, so loc[...,0] is x (width) and
+loc[...,1] is y (height), both in [0,1] inside the image.
+
+Readings of what the pages leave open (each is documented with the repository):
+
+* R1 pixel centres. (0,0) and (1,1) are the image's outer corners (section
+  "Multi-scale deformable attention"), and phi_l multiplies by the level's
+  width/height. A pixel is then a unit cell, pixel j's centre is at (j+0.5)/W,
+  and the index-space coordinate is x = loc_x * W - 0.5 (likewise y with H).
+* R2 zero padding. Offsets are unconstrained; the pages never say what lies
+  outside the map. A corner outside the map reads 0, so a sample with
+  -1 <= x < W and -1 <= y < H gets partial weight and any other contributes 0.
+* R3 one rounding of the index coordinate. x is rounded once to binary32 (the
+  GPU forms it with one fused multiply-add); everything after x is float64.
+  For float32 loc with |loc| >= 2^-30 and W < 2^24 the float64 product and
+  difference below are exact, so the single cast equals a correctly rounded
+  fused multiply-add wherever floor(x) could change.
+* R4 the floor rule at kinks. Bilinear interpolation is not differentiable in x
+  at integer x; the oracle uses x0 = floor(x) everywhere, i.e. the
+  right-derivative, including at x = -1 (which the in-map test keeps).
+* R5 level flattening. Row of pixel (i, j) of level l is level_start[l] + i*W_l + j.
+* R6 weights are used as given: no renormalisation and no softmax inside.
+
+Gradients (page "Deformable Attention", differentiability of the bilinear
+sampling, gradients flowing through the interpolation grid to the offsets):
+out is linear in A and in the value map, and piecewise bilinear in (x, y); the
+chain rule through x = loc_x*W - 0.5 gives d/dloc_x = W * d/dx (the rounding in
+R3 is taken to have derivative 1).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# Corner order used throughout: (dy, dx) offsets from (y0, x0).
+_CORNERS = ((0, 0), (0, 1), (1, 0), (1, 1))
+
+
+def pixel_coordinate(loc, size, round_coords=True):
+    """Index-space coordinate of a normalised location on an axis of ``size``
+    pixels: loc*size - 0.5 (reading R1), rounded once to binary32 (R3) unless
+    ``round_coords`` is False (used by finite-difference checks)."""
+    t = np.asarray(loc, dtype=np.float64) * float(size) - 0.5
+    if round_coords:
+        t = t.astype(np.float32).astype(np.float64)
+    return t
+
+
+def _check(value, spatial_shapes, level_start, loc, attn):
+    value = np.asarray(value)
+    spatial_shapes = np.asarray(spatial_shapes, dtype=np.int64)
+    level_start = np.asarray(level_start, dtype=np.int64)
+    N, S, M, D = value.shape
+    L = spatial_shapes.shape[0]
+    assert spatial_shapes.shape == (L, 2) and level_start.shape == (L,)
+    assert loc.shape[0] == N and loc.shape[2] == M and loc.shape[3] == L and loc.shape[5] == 2
+    assert attn.shape == loc.shape[:5]
+    for l in range(L):
+        h, w = spatial_shapes[l]
+        assert h >= 1 and w >= 1 and 0 <= level_start[l] and level_start[l] + h * w <= S
+    return spatial_shapes, level_start
+
+
+def _bilinear_terms(value, n, m, px, py, H, W, s0, round_coords):
+    """For P samples on one level (batch index n[P], head m[P], normalised
+    location (px, py)[P]), return the fractional parts a, b, the in-map flag of
+    each sample, and the four corner reads Vpad[c] (each [P, D], zero where the
+    corner is outside the map, reading R2) together with each corner's row and
+    in-map flag."""
+    x = pixel_coordinate(px, W, round_coords)
+    y = pixel_coordinate(py, H, round_coords)
+    # NaN fails every comparison, so a NaN location contributes nothing.
+    inside = (x >= -1.0) & (x < W) & (y >= -1.0) & (y < H)
+    x0 = np.floor(np.where(inside, x, 0.0))
+    y0 = np.floor(np.where(inside, y, 0.0))
+    a = np.where(inside, x, 0.0) - x0
+    b = np.where(inside, y, 0.0) - y0
+    reads, rows, oks = [], [], []
+    D = value.shape[3]
+    for dy, dx in _CORNERS:
+        i = (y0 + dy).astype(np.int64)
+        j = (x0 + dx).astype(np.int64)
+        ok = inside & (i >= 0) & (i < H) & (j >= 0) & (j < W)
+        row = s0 + np.where(ok, i * W + j, 0)
+        v = np.where(ok[:, None], value[n, row, m, :], 0.0) if len(n) else np.zeros((0, D))
+        reads.append(v)
+        rows.append(row)
+        oks.append(ok)
+    return a, b, inside, reads, rows, oks
+
+
+def _pairs_all(N, Lq, M):
+    n, q, m = np.meshgrid(np.arange(N), np.arange(Lq), np.arange(M), indexing="ij")
+    return n.ravel(), q.ravel(), m.ravel()
+
+
+def msda_forward(value, spatial_shapes, level_start, loc, attn, pairs=None,
+                 round_coords=True, chunk=1 << 16):
+    """out[n,q,m,:] for every (n, q, m), or for the (n[P], q[P], m[P]) listed in
+    ``pairs`` (then the result is [P, D]). float64 throughout."""
+    spatial_shapes, level_start = _check(value, spatial_shapes, level_start, loc, attn)
+    value = np.asarray(value, dtype=np.float64)
+    N, S, M, D = value.shape
+    Lq, L, K = loc.shape[1], loc.shape[3], loc.shape[4]
+    full = pairs is None
+    pn, pq, pm = _pairs_all(N, Lq, M) if full else (np.asarray(p, dtype=np.int64) for p in pairs)
+    P = len(pn)
+    out = np.zeros((P, D), dtype=np.float64)
+    for c0 in range(0, P, chunk):
+        n, q, m = pn[c0:c0 + chunk], pq[c0:c0 + chunk], pm[c0:c0 + chunk]
+        acc = np.zeros((len(n), D), dtype=np.float64)
+        for l in range(L):
+            H, W = int(spatial_shapes[l, 0]), int(spatial_shapes[l, 1])
+            s0 = int(level_start[l])
+            for k in range(K):
+                A = np.asarray(attn[n, q, m, l, k], dtype=np.float64)
+                a, b, inside, V, _, _ = _bilinear_terms(
+                    value, n, m, loc[n, q, m, l, k, 0], loc[n, q, m, l, k, 1], H, W, s0, round_coords)
+                samp = (((1 - b) * (1 - a))[:, None] * V[0] + ((1 - b) * a)[:, None] * V[1]
+                        + (b * (1 - a))[:, None] * V[2] + (b * a)[:, None] * V[3])
+                acc += np.where(inside, A, 0.0)[:, None] * samp
+        out[c0:c0 + chunk] = acc
+    return out.reshape(N, Lq, M, D) if full else out
+
+
+def msda_backward(value, spatial_shapes, level_start, loc, attn, grad_out, pairs=None,
+                  round_coords=True, chunk=1 << 16, with_grad_value=True):
+    """Gradients of sum(grad_out * out) with respect to value, loc and attn.
+
+    Returns (grad_value [N,S,M,D] or None, grad_loc, grad_attn); with ``pairs``
+    the last two are [P,L,K,2] and [P,L,K] for the listed pairs and grad_value
+    (if requested) holds only their contributions."""
+    spatial_shapes, level_start = _check(value, spatial_shapes, level_start, loc, attn)
+    value = np.asarray(value, dtype=np.float64)
+    grad_out = np.asarray(grad_out, dtype=np.float64)
+    N, S, M, D = value.shape
+    Lq, L, K = loc.shape[1], loc.shape[3], loc.shape[4]
+    full = pairs is None
+    pn, pq, pm = _pairs_all(N, Lq, M) if full else (np.asarray(p, dtype=np.int64) for p in pairs)
+    P = len(pn)
+    grad_value = np.zeros((N, S, M, D), dtype=np.float64) if with_grad_value else None
+    grad_loc = np.zeros((P, L, K, 2), dtype=np.float64)
+    grad_attn = np.zeros((P, L, K), dtype=np.float64)
+    for c0 in range(0, P, chunk):
+        n, q, m = pn[c0:c0 + chunk], pq[c0:c0 + chunk], pm[c0:c0 + chunk]
+        G = grad_out[n, q, m, :]
+        for l in range(L):
+            H, W = int(spatial_shapes[l, 0]), int(spatial_shapes[l, 1])
+            s0 = int(level_start[l])
+            for k in range(K):
+                A = np.asarray(attn[n, q, m, l, k], dtype=np.float64)
+                a, b, inside, V, rows, oks = _bilinear_terms(
+                    value, n, m, loc[n, q, m, l, k, 0], loc[n, q, m, l, k, 1], H, W, s0, round_coords)
+                w = ((1 - b) * (1 - a), (1 - b) * a, b * (1 - a), b * a)
+                samp = sum(wc[:, None] * Vc for wc, Vc in zip(w, V))
+                # out is linear in A: d out / d A = the bilinear sample.
+                grad_attn[c0:c0 + chunk, l, k] = np.where(inside, (G * samp).sum(1), 0.0)
+                # d sample / d x and d / d y of the bilinear form (right-derivative, R4).
+                dsdx = (1 - b)[:, None] * (V[1] - V[0]) + b[:, None] * (V[3] - V[2])
+                dsdy = (1 - a)[:, None] * (V[2] - V[0]) + a[:, None] * (V[3] - V[1])
+                grad_loc[c0:c0 + chunk, l, k, 0] = np.where(inside, A * W * (G * dsdx).sum(1), 0.0)
+                grad_loc[c0:c0 + chunk, l, k, 1] = np.where(inside, A * H * (G * dsdy).sum(1), 0.0)
+                if with_grad_value:
+                    # out is linear in the value map: each in-map corner receives A * w_c * G.
+                    for wc, row, ok in zip(w, rows, oks):
+                        sel = ok & inside
+                        np.add.at(grad_value, (n[sel], row[sel], m[sel]),
+                                  (A * wc)[sel, None] * G[sel])
+    if full:
+        grad_loc = grad_loc.reshape(N, Lq, M, L, K, 2)
+        grad_attn = grad_attn.reshape(N, Lq, M, L, K)
+    return grad_value, grad_loc, grad_attn
+
+
+def msda_grad_value_rows(value, spatial_shapes, level_start, loc, attn, grad_out, rows,
+                         round_coords=True, chunk=1 << 16):
+    """grad_value at the listed (n[R], s[R], m[R]) rows only ([R, D]), summing
+    every sample corner that lands on them. Scans all points once; used where the
+    full scatter would be too slow."""
+    spatial_shapes, level_start = _check(value, spatial_shapes, level_start, loc, attn)
+    value = np.asarray(value, dtype=np.float64)
+    N, S, M, D = value.shape
+    Lq, L, K = loc.shape[1], loc.shape[3], loc.shape[4]
+    rn, rs, rm = (np.asarray(r, dtype=np.int64) for r in rows)
+    keys = (rn * S + rs) * M + rm
+    order = np.argsort(keys, kind="stable")
+    skeys = keys[order]
+    res = np.zeros((len(keys), D), dtype=np.float64)
+    pn, pq, pm = _pairs_all(N, Lq, M)
+    for c0 in range(0, len(pn), chunk):
+        n, q, m = pn[c0:c0 + chunk], pq[c0:c0 + chunk], pm[c0:c0 + chunk]
+        for l in range(L):
+            H, W = int(spatial_shapes[l, 0]), int(spatial_shapes[l, 1])
+            s0 = int(level_start[l])
+            for k in range(K):
+                px, py = loc[n, q, m, l, k, 0], loc[n, q, m, l, k, 1]
+                x = pixel_coordinate(px, W, round_coords)
+                y = pixel_coordinate(py, H, round_coords)
+                inside = (x >= -1.0) & (x < W) & (y >= -1.0) & (y < H)
+                x0 = np.floor(np.where(inside, x, 0.0))
+                y0 = np.floor(np.where(inside, y, 0.0))
+                a = np.where(inside, x, 0.0) - x0
+                b = np.where(inside, y, 0.0) - y0
+                A = np.asarray(attn[n, q, m, l, k], dtype=np.float64)
+                w = ((1 - b) * (1 - a), (1 - b) * a, b * (1 - a), b * a)
+                for (dy, dx), wc in zip(_CORNERS, w):
+                    i = (y0 + dy).astype(np.int64)
+                    j = (x0 + dx).astype(np.int64)
+                    ok = inside & (i >= 0) & (i < H) & (j >= 0) & (j < W)
+                    key = (n * S + s0 + np.where(ok, i * W + j, 0)) * M + m
+                    pos = np.searchsorted(skeys, key)
+                    hit = ok & (pos < len(skeys))
+                    hit[hit] = skeys[pos[hit]] == key[hit]
+                    if not hit.any():
+                        continue
+                    contrib = (A * wc)[hit, None] * np.asarray(grad_out[n[hit], q[hit], m[hit], :], dtype=np.float64)
+                    # Duplicate requested rows share one slot; spread back below.
+                    np.add.at(res, order[pos[hit]], contrib)
+    # Rows requested twice: copy the accumulated value to every duplicate.
+    first = np.searchsorted(skeys, keys)
+    return res[order[first]]

@@ -1,0 +1,376 @@
+"""Pins of the fp64 oracle to facts outside itself (CPU only).
+
+Each test ties one part of the oracle to something it does not compute itself:
+the worked example printed on page "Deformable DETR Samples Sparse Points",
+closed forms, invariants of the equation, a dense brute force written without
+floor or padding logic, a library bilinear sampler, finite differences and exact
+rational arithmetic.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+from oracle import msda_backward, msda_forward, msda_grad_value_rows, pixel_coordinate
+from tests.dense_reference import (dense_forward_backward, exact_index_coordinate,
+                                   round_fraction_to_f32)
+from workloads import init_pattern_workload, level_starts, uniform_workload
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _single(value_hw, loc_xy, weights, M=1, D=1):
+    """Helper: one image, one query, one level, K = len(weights) samples."""
+    H, W = value_hw.shape[:2]
+    value = value_hw.reshape(1, H * W, M, D)
+    K = len(weights)
+    loc = np.asarray(loc_xy, dtype=np.float32).reshape(1, 1, M, 1, K, 2)
+    attn = np.asarray(weights, dtype=np.float32).reshape(1, 1, M, 1, K)
+    return value, np.array([[H, W]]), np.array([0]), loc, attn
+
+
+# --- P1: the printed worked example -------------------------------------------------------
+
+def _golden():
+    with open(os.path.join(GOLDEN, "worked_example.json")) as f:
+        return json.load(f)
+
+
+def test_worked_example_offsets_add_up():
+    g = _golden()
+    ref = np.array(g["reference_point"])
+    np.testing.assert_allclose(ref + np.array(g["offsets"]), np.array(g["locations"]), atol=1e-12)
+    np.testing.assert_allclose(np.array(g["weights"]) * np.array(g["sampled_values"]),
+                               g["products"], atol=1e-12)
+
+
+def test_worked_example_pixel_centres():
+    """The page's four samples fall next to the 2x2 pixel block around (14,14) of the
+    28x28 map; reading those pixels at their centres with the page's weights blends
+    their values to the printed 0.70."""
+    g = _golden()
+    H, W = g["map_hw"]
+    rng = np.random.default_rng(0)
+    vmap = rng.uniform(-1, 1, (H, W))
+    pix = [(14, 14), (13, 14), (13, 13), (14, 13)]  # (x, y) nearest pixel of each printed location
+    for (x, y), v in zip(pix, g["sampled_values"]):
+        vmap[y, x] = v
+    # nearest-pixel claim: each printed location is within one pixel of the chosen centre
+    for (x, y), (lx, ly) in zip(pix, g["locations"]):
+        assert abs(lx * W - 0.5 - x) <= 0.5 + 1e-9 and abs(ly * H - 0.5 - y) <= 0.5 + 1e-9
+    loc = [((x + 0.5) / W, (y + 0.5) / H) for x, y in pix]
+    out = msda_forward(*_single(vmap, loc, g["weights"]))
+    assert abs(out[0, 0, 0, 0] - g["blend"]) < 1e-6  # weights are float32 inputs
+
+
+def test_worked_example_page_locations():
+    """At the page's own fractional locations: on a map that holds a bilinear surface
+    f = c0 + c1 x + c2 y + c3 xy (pixel coordinates), bilinear interpolation is exact,
+    so choosing c with f(sample_k) = printed value_k makes the blend exactly 0.70."""
+    g = _golden()
+    H, W = g["map_hw"]
+    xs = [exact_index_coordinate(lx, W) for lx, _ in g["locations"]]
+    ys = [exact_index_coordinate(ly, H) for _, ly in g["locations"]]
+    Amat = np.array([[1.0, x, y, x * y] for x, y in zip(xs, ys)])
+    c = np.linalg.solve(Amat, np.array(g["sampled_values"]))
+    ii, jj = np.meshgrid(np.arange(H), np.arange(W), indexing="ij")
+    vmap = c[0] + c[1] * jj + c[2] * ii + c[3] * jj * ii
+    out = msda_forward(*_single(vmap, g["locations"], g["weights"]))
+    w32 = np.asarray(g["weights"], dtype=np.float32).astype(np.float64)
+    expect = float(np.dot(w32, g["sampled_values"]))
+    assert abs(expect - g["blend"]) < 1e-7
+    assert abs(out[0, 0, 0, 0] - expect) < 1e-10
+
+
+# --- R3: the single binary32 rounding of the index coordinate -------------------------------
+
+def test_pixel_coordinate_is_one_correct_rounding():
+    rng = np.random.default_rng(11)
+    locs = np.concatenate([
+        rng.uniform(-0.2, 1.2, 4000),
+        # adversarial: locations whose index coordinate is within an ulp of an integer
+        ((np.arange(-3, 170) + 0.5) / 167.0),
+        np.nextafter(((np.arange(-3, 170) + 0.5) / 167.0).astype(np.float32), np.float32(2)),
+        np.nextafter(((np.arange(-3, 170) + 0.5) / 167.0).astype(np.float32), np.float32(-2)),
+    ]).astype(np.float32)
+    for size in (13, 16, 21, 42, 84, 100, 167):
+        got = pixel_coordinate(locs, size)
+        for lv, gv in zip(locs[::7], got[::7]):
+            ex = Fraction(float(lv)) * size - Fraction(1, 2)
+            if ex == 0 or abs(ex) < Fraction(1, 2 ** 100):
+                continue
+            assert gv == round_fraction_to_f32(ex)
+
+
+# --- P2: constant maps ----------------------------------------------------------------------
+
+def _tent_mass(t, n):
+    """In-map share of a unit tent centred at index coordinate t on an axis of n pixels."""
+    return np.clip(np.minimum(t + 1.0, n - t), 0.0, 1.0)
+
+
+def test_constant_map_inside_returns_constant():
+    w = uniform_workload(N=2, shapes=((7, 9), (4, 5)), Lq=11, M=3, D=4, K=3, seed=21, lo=0.2, hi=0.8)
+    w.value[:] = 0.625
+    out = msda_forward(w.value, w.spatial_shapes, w.level_start, w.loc, w.attn)
+    expect = 0.625 * w.attn.astype(np.float64).sum(axis=(3, 4))
+    np.testing.assert_allclose(out, np.broadcast_to(expect[..., None], out.shape), rtol=0, atol=1e-12)
+
+
+def test_constant_map_border_mass_closed_form():
+    w = uniform_workload(N=1, shapes=((6, 10), (3, 4)), Lq=40, M=2, D=2, K=4, seed=22, lo=-0.4, hi=1.4)
+    w.value[:] = -1.5
+    out = msda_forward(w.value, w.spatial_shapes, w.level_start, w.loc, w.attn, round_coords=False)
+    expect = np.zeros(out.shape[:3])
+    for l, (H, W) in enumerate(w.spatial_shapes):
+        x = w.loc[:, :, :, l, :, 0].astype(np.float64) * W - 0.5
+        y = w.loc[:, :, :, l, :, 1].astype(np.float64) * H - 0.5
+        expect += (w.attn[:, :, :, l, :] * _tent_mass(x, W) * _tent_mass(y, H)).sum(-1)
+    np.testing.assert_allclose(out, -1.5 * np.broadcast_to(expect[..., None], out.shape), atol=1e-12)
+
+
+# --- P3: pixel-centre reads ----------------------------------------------------------------
+
+def test_pixel_centres_read_exact_pixels():
+    rng = np.random.default_rng(3)
+    H, W, M, D, K = 16, 8, 2, 3, 5
+    value = rng.standard_normal((1, H * W, M, D))
+    ii = rng.integers(0, H, (1, 1, M, 1, K))
+    jj = rng.integers(0, W, (1, 1, M, 1, K))
+    loc = np.stack([(jj + 0.5) / W, (ii + 0.5) / H], axis=-1).astype(np.float32)
+    attn = rng.uniform(0, 1, (1, 1, M, 1, K)).astype(np.float32)
+    out = msda_forward(value, [[H, W]], [0], loc, attn)
+    for m in range(M):
+        expect = sum(attn[0, 0, m, 0, k] * value[0, ii[0, 0, m, 0, k] * W + jj[0, 0, m, 0, k], m]
+                     for k in range(K))
+        np.testing.assert_allclose(out[0, 0, m], expect, atol=1e-14)
+
+
+# --- P4: border closed forms -----------------------------------------------------------------
+
+def test_border_closed_forms():
+    rng = np.random.default_rng(4)
+    H, W = 8, 16
+    vmap = rng.standard_normal((H, W))
+    i = 5
+    cases = [((0.0, 0.0), 0.25 * vmap[0, 0]),
+             ((1.0, 1.0), 0.25 * vmap[H - 1, W - 1]),
+             ((0.0, (i + 0.5) / H), 0.5 * vmap[i, 0]),
+             ((1.0, (i + 0.5) / H), 0.5 * vmap[i, W - 1]),
+             ((-2.0 / W, 0.5), 0.0),          # x = -2.5: beyond one pixel outside
+             ((0.5, 1.0 + 1.0 / H), 0.0),     # y = H + 0.5
+             ((1.0 + 0.5 / W, 0.5), 0.0)]     # x = W exactly: outside by the half-open rule
+    for (lx, ly), expect in cases:
+        args = _single(vmap, [(lx, ly)], [0.8])
+        out = msda_forward(*args)
+        assert abs(out[0, 0, 0, 0] - 0.8 * expect) < 1e-7, (lx, ly)
+        gv, gl, ga = msda_backward(*args, grad_out=np.ones((1, 1, 1, 1)))
+        if expect == 0.0:
+            assert np.all(gv == 0) and np.all(gl == 0) and np.all(ga == 0)
+
+
+# --- P5: dense-grid brute force ----------------------------------------------------------------
+
+@pytest.mark.parametrize("seed", [31, 32])
+def test_dense_bruteforce_forward_backward(seed):
+    w = uniform_workload(N=2, shapes=((5, 7), (3, 4), (2, 2)), Lq=6, M=3, D=4, K=3, seed=seed,
+                         lo=-0.15, hi=1.15, with_grad=True)
+    args = (w.value, w.spatial_shapes, w.level_start, w.loc, w.attn)
+    out, gv_d, gl_d, ga_d = dense_forward_backward(*args, grad_out=w.grad_out)
+    np.testing.assert_allclose(msda_forward(*args), out, atol=1e-13)
+    gv, gl, ga = msda_backward(*args, grad_out=w.grad_out)
+    np.testing.assert_allclose(gv, gv_d, atol=1e-12)
+    np.testing.assert_allclose(ga, ga_d, atol=1e-12)
+    np.testing.assert_allclose(gl, gl_d, atol=1e-10)
+
+
+def test_dense_bruteforce_on_kinks():
+    """P10: the compass initialisation puts every sample on a pixel centre, where the
+    location gradient jumps; the oracle must give the right-derivative there."""
+    w = init_pattern_workload(N=1, shape=(8, 8), M=8, D=3, K=2, seed=7)
+    w = _subset_queries(w, np.arange(0, 64, 5))
+    args = (w.value, w.spatial_shapes, w.level_start, w.loc, w.attn)
+    x = w.loc[..., 0].astype(np.float64) * 8 - 0.5
+    assert np.all(x == np.round(x))  # every sample exactly on a kink
+    out, gv_d, gl_d, ga_d = dense_forward_backward(*args, grad_out=w.grad_out)
+    gv, gl, ga = msda_backward(*args, grad_out=w.grad_out)
+    np.testing.assert_allclose(msda_forward(*args), out, atol=1e-13)
+    np.testing.assert_allclose(gl, gl_d, atol=1e-11)
+    np.testing.assert_allclose(gv, gv_d, atol=1e-12)
+    np.testing.assert_allclose(ga, ga_d, atol=1e-12)
+    # and the right-derivative is what a forward difference sees
+    h = 2.0 ** -20
+    for axis in (0, 1):
+        lp = w.loc.astype(np.float64).copy()
+        lp[..., axis] += h
+        fd = ((msda_forward(w.value, w.spatial_shapes, w.level_start, lp, w.attn, round_coords=False)
+               - out) * w.grad_out).sum()
+        np.testing.assert_allclose(fd / h, gl[..., axis].sum(), rtol=1e-6, atol=1e-8)
+
+
+def _subset_queries(w, qs):
+    w.loc = np.ascontiguousarray(w.loc[:, qs])
+    w.attn = np.ascontiguousarray(w.attn[:, qs])
+    w.grad_out = np.ascontiguousarray(w.grad_out[:, qs])
+    return w
+
+
+# --- P6: a library bilinear sampler ----------------------------------------------------------------
+
+def test_single_sample_matches_torch_grid_sample():
+    """L=1, K=1, A=1 is a plain bilinear sample (the deformable-convolution special
+    case on page "Deformable DETR"); compare with torch's CPU grid_sample in float64,
+    zero padding, align_corners=False, grid = 2*loc - 1."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(5)
+    H, W, D, P = 6, 9, 3, 200
+    vmap = rng.standard_normal((H, W, D))
+    loc = rng.uniform(-0.2, 1.2, (P, 2)).astype(np.float32)
+    x = loc[:, 0].astype(np.float64) * W - 0.5
+    y = loc[:, 1].astype(np.float64) * H - 0.5
+    off_kink = (np.abs(x - np.round(x)) > 1e-4) & (np.abs(y - np.round(y)) > 1e-4)
+    value = vmap.reshape(1, H * W, 1, D)
+    locs = loc.reshape(1, P, 1, 1, 1, 2)
+    attn = np.ones((1, P, 1, 1, 1), dtype=np.float32)
+    G = rng.standard_normal((1, P, 1, D))
+    out = msda_forward(value, [[H, W]], [0], locs, attn, round_coords=False)
+    gv, gl, _ = msda_backward(value, [[H, W]], [0], locs, attn, G, round_coords=False)
+    inp = torch.tensor(vmap.transpose(2, 0, 1)[None], dtype=torch.float64, requires_grad=True)
+    grid = torch.tensor(2.0 * loc.astype(np.float64) - 1.0, dtype=torch.float64).reshape(1, 1, P, 2)
+    grid.requires_grad_(True)
+    ref = torch.nn.functional.grid_sample(inp, grid, mode="bilinear", padding_mode="zeros",
+                                          align_corners=False)  # [1, D, 1, P]
+    np.testing.assert_allclose(out[0, :, 0, :], ref[0, :, 0, :].T.detach().numpy(), atol=1e-12)
+    (ref[0, :, 0, :].T * torch.tensor(G[0, :, 0, :])).sum().backward()
+    np.testing.assert_allclose(gv.reshape(H, W, D), inp.grad[0].numpy().transpose(1, 2, 0), atol=1e-12)
+    g_grid = grid.grad.numpy().reshape(P, 2)
+    np.testing.assert_allclose(gl.reshape(P, 2)[off_kink], 2.0 * g_grid[off_kink], atol=1e-10)
+
+
+# --- P7: finite differences ----------------------------------------------------------------------
+
+def test_finite_differences():
+    w = uniform_workload(N=1, shapes=((6, 8), (3, 5)), Lq=5, M=2, D=3, K=2, seed=41,
+                         lo=-0.1, hi=1.1, with_grad=True)
+    loc = w.loc.astype(np.float64)
+    args = (w.value, w.spatial_shapes, w.level_start)
+    G = w.grad_out.astype(np.float64)
+    gv, gl, ga = msda_backward(*args, loc, w.attn, G, round_coords=False)
+
+    def f(value=w.value, loc=loc, attn=w.attn):
+        return (msda_forward(value, w.spatial_shapes, w.level_start, loc, attn, round_coords=False) * G).sum()
+
+    rng = np.random.default_rng(0)
+    # value and attn: the output is linear in each, so any step is exact up to rounding
+    for _ in range(10):
+        idx = tuple(rng.integers(0, s) for s in w.value.shape)
+        v2 = w.value.astype(np.float64).copy()
+        v2[idx] += 0.5
+        assert abs((f(value=v2) - f()) / 0.5 - gv[idx]) < 1e-10
+        idx = tuple(rng.integers(0, s) for s in w.attn.shape)
+        a2 = w.attn.astype(np.float64).copy()
+        a2[idx] += 0.5
+        assert abs((f(attn=a2) - f()) / 0.5 - ga[idx]) < 1e-10
+    # loc: central differences away from kinks
+    checked = 0
+    for idx in np.ndindex(*loc.shape):
+        l = idx[3]
+        size = w.spatial_shapes[l][1 - idx[5]]  # x uses W, y uses H
+        t = loc[idx] * size - 0.5
+        if abs(t - np.round(t)) < 1e-4:
+            continue
+        h = 1e-6 / size
+        lp, lm = loc.copy(), loc.copy()
+        lp[idx] += h
+        lm[idx] -= h
+        fd = (f(loc=lp) - f(loc=lm)) / (2 * h)
+        assert abs(fd - gl[idx]) < 1e-6 * max(1.0, abs(gl[idx])), (idx, fd, gl[idx])
+        checked += 1
+    assert checked > 50
+
+
+# --- P8: adjoint identities ----------------------------------------------------------------------
+
+def test_adjoint_identities():
+    w = uniform_workload(N=2, shapes=((9, 11), (5, 6)), Lq=30, M=4, D=5, K=3, seed=51,
+                         lo=-0.1, hi=1.1, with_grad=True)
+    args = (w.value, w.spatial_shapes, w.level_start, w.loc, w.attn)
+    out = msda_forward(*args)
+    gv, gl, ga = msda_backward(*args, grad_out=w.grad_out)
+    lhs = (w.grad_out.astype(np.float64) * out).sum()
+    assert abs(lhs - (gv * w.value).sum()) < 1e-10 * max(1, abs(lhs))
+    assert abs(lhs - (ga * w.attn).sum()) < 1e-10 * max(1, abs(lhs))
+
+
+# --- P9: invariants --------------------------------------------------------------------------------
+
+def test_invariants_heads_levels_batch():
+    w = uniform_workload(N=3, shapes=((6, 7), (3, 4)), Lq=9, M=4, D=3, K=2, seed=61, lo=-0.1, hi=1.1)
+    args = (w.value, w.spatial_shapes, w.level_start)
+    out = msda_forward(*args, w.loc, w.attn)
+    # head permutation equivariance
+    perm = np.array([2, 0, 3, 1])
+    outp = msda_forward(w.value[:, :, perm], w.spatial_shapes, w.level_start, w.loc[:, :, perm],
+                        w.attn[:, :, perm])
+    np.testing.assert_allclose(outp, out[:, :, perm], atol=1e-14)
+    # level additivity
+    acc = 0
+    for l in range(2):
+        a = np.zeros_like(w.attn)
+        a[:, :, :, l] = w.attn[:, :, :, l]
+        acc = acc + msda_forward(*args, w.loc, a)
+    np.testing.assert_allclose(acc, out, atol=1e-13)
+    # batch independence
+    out1 = msda_forward(w.value[1:2], w.spatial_shapes, w.level_start, w.loc[1:2], w.attn[1:2])
+    np.testing.assert_allclose(out1, out[1:2], atol=1e-14)
+
+
+def test_transpose_and_translation():
+    rng = np.random.default_rng(71)
+    H, W, M, D, K, Lq = 8, 16, 2, 3, 4, 7  # non-square, powers of two: exact coordinates
+    vmap = rng.standard_normal((H, W, M, D))
+    # locations on a 1/1024 lattice keep every coordinate exact in binary32
+    loc = (rng.integers(-50, 1074, (1, Lq, M, 1, K, 2)) / 1024.0).astype(np.float32)
+    attn = rng.uniform(0, 1, (1, Lq, M, 1, K)).astype(np.float32)
+    out = msda_forward(vmap.reshape(1, H * W, M, D), [[H, W]], [0], loc, attn)
+    # transposed map with swapped location components
+    vt = vmap.transpose(1, 0, 2, 3).reshape(1, W * H, M, D)
+    outt = msda_forward(vt, [[W, H]], [0], loc[..., ::-1].copy(), attn)
+    np.testing.assert_allclose(outt, out, atol=1e-14)
+    # translation: shift the map one pixel right (zero column enters on the left) and the
+    # locations by one pixel; samples that stay clear of the new border are unchanged
+    vs = np.zeros((H, W + 1, M, D))
+    vs[:, 1:] = vmap
+    loc_s = loc.astype(np.float64).copy()
+    loc_s[..., 0] = (loc_s[..., 0] * W + 1.0) / (W + 1)
+    outs = msda_forward(vs.reshape(1, H * (W + 1), M, D), [[H, W + 1]], [0], loc_s, attn,
+                        round_coords=False)
+    np.testing.assert_allclose(outs, out, atol=1e-12)
+
+
+# --- helpers used at full size agree with the full computation -------------------------------------
+
+def test_pair_subset_and_row_subset_agree_with_full():
+    w = uniform_workload(N=2, shapes=((7, 9), (4, 5)), Lq=13, M=3, D=4, K=3, seed=81, lo=-0.1, hi=1.1,
+                         with_grad=True)
+    args = (w.value, w.spatial_shapes, w.level_start, w.loc, w.attn)
+    out = msda_forward(*args)
+    gv, gl, ga = msda_backward(*args, grad_out=w.grad_out)
+    rng = np.random.default_rng(1)
+    pn, pq, pm = rng.integers(0, 2, 20), rng.integers(0, 13, 20), rng.integers(0, 3, 20)
+    np.testing.assert_allclose(msda_forward(*args, pairs=(pn, pq, pm)), out[pn, pq, pm], atol=1e-14)
+    _, gl_p, ga_p = msda_backward(*args, grad_out=w.grad_out, pairs=(pn, pq, pm), with_grad_value=False)
+    np.testing.assert_allclose(gl_p, gl[pn, pq, pm], atol=1e-14)
+    np.testing.assert_allclose(ga_p, ga[pn, pq, pm], atol=1e-14)
+    S = w.value.shape[1]
+    rn, rs, rm = rng.integers(0, 2, 30), rng.integers(0, S, 30), rng.integers(0, 3, 30)
+    rn[1], rs[1], rm[1] = rn[0], rs[0], rm[0]  # a duplicate request
+    got = msda_grad_value_rows(*args, w.grad_out, (rn, rs, rm))
+    np.testing.assert_allclose(got, gv[rn, rs, rm], atol=1e-13)
+
+
+def test_level_starts_layout():
+    starts, S = level_starts(((100, 167), (50, 84), (25, 42), (13, 21)))
+    assert list(starts) == [0, 16700, 20900, 21950] and S == 22223
