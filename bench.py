@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Throughput of the MSDA sampling core (forward + backward) on one MI355X.
+
+One step = msda_forward then msda_backward on the encoder-shape workload: one
+800x1333 image's four levels 100x167, 50x84, 25x42, 13x21 (S = Lq = 22223),
+M=8 heads, D=32 channels per head (C=256), K=4 points, fp32, every pixel a
+query with N(0, 2 px) offsets and softmax weights (synthetic stand-in for
+COCO feature maps). Inputs are resident in HBM before timing. Several buffer
+sets (inputs and outputs) are cycled so that no step finds its data in the
+256 MB Infinity Cache left behind by the previous one.
+
+Prints one JSON line: sampled points/s (N*Lq*M*L*K per step / step time),
+per-pass timings from HIP events on the launch stream, the HBM roofline of
+the dominant kernel and the fp64 CPU oracle's rate on a bounded sample.
+"""
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
+KERNEL_SRC = os.path.join(ROOT, "scale_deformable_attention_msda_amd", "csrc", "msda_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "msda_encoder_fwd_bwd_hbm_traffic.md")
+
+
+def kernel_source_hash():
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it was
+    taken on the current kernel source; None otherwise."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    text = open(TRAFFIC_FILE).read()
+    m = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    if not m or m.group(1) != kernel_source_hash():
+        return None
+    out = {}
+    for key in ("fwd", "bwd"):
+        mm = re.search(rf"traffic_bytes_{key}:\s*([0-9.eE+]+)", text)
+        if mm:
+            out[key] = float(mm.group(1))
+    return out or None
+
+
+def cpu_baseline(w, seconds):
+    """The fp64 oracle, as it stands, on the first P (n, q, m) pairs of the same
+    workload: forward plus backward (grad_value scatter included)."""
+    import numpy as np
+
+    from oracle import msda_backward, msda_forward
+
+    d = w.dims
+    args = (w.value, w.spatial_shapes, w.level_start, w.loc, w.attn)
+
+    def run(P):
+        idx = np.arange(P)
+        n = idx // (d["Lq"] * d["M"])
+        q = (idx // d["M"]) % d["Lq"]
+        m = idx % d["M"]
+        t0 = time.perf_counter()
+        msda_forward(*args, pairs=(n, q, m))
+        msda_backward(*args, w.grad_out, pairs=(n, q, m), with_grad_value=True)
+        return time.perf_counter() - t0
+
+    P = 2048
+    t = run(P)
+    P = int(min(d["N"] * d["Lq"] * d["M"], max(P, P * seconds / max(t, 1e-3))))
+    t = run(P)
+    pts = P * d["L"] * d["K"]
+    return {"value": pts / t, "unit": "sampled points/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {P} (n,q,m) pairs = {pts} points of the same workload, forward + "
+                      f"backward in float64 NumPy, single-threaded ({t:.1f} s)",
+            "host_cpus_available": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--rotate", type=int, default=4, help="buffer sets cycled across steps")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 256 MiB device copy (HBM counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build measures one GPU only; the sampling core needs no "
+                                   "collective and multi-GPU runs are not part of it",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import scale_deformable_attention_msda_amd as msda
+    from workloads import config_workload
+
+    w = config_workload("encoder_fwd", with_grad=True)
+    d = w.dims
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pts = w.points
+    U = d["N"] * d["S"] * d["M"] * d["D"] * 4  # bytes of one fp32 value map
+    assert d["Lq"] * d["M"] * d["D"] * 4 == U
+    # algorithmic bytes: every input read once, every output written once
+    # (value counted in full: in this encoder workload every row is sampled)
+    b_fwd = U + U + U // 2 + U            # value, loc, attn, out
+    b_bwd = U + U + U + U // 2 + U + U + U // 2  # value, grad_out, loc, attn | grad_value, grad_loc, grad_attn
+
+    host = dict(value=torch.from_numpy(w.value), loc=torch.from_numpy(w.loc),
+                attn=torch.from_numpy(w.attn), grad_out=torch.from_numpy(w.grad_out))
+    sets = []
+    for _ in range(args.rotate):
+        s = {k: v.to(dev) for k, v in host.items()}
+        s["out"] = torch.empty((d["N"], d["Lq"], d["M"], d["D"]), dtype=torch.float32, device=dev)
+        s["gv"] = torch.empty_like(s["value"])
+        s["gl"] = torch.empty_like(s["loc"])
+        s["ga"] = torch.empty_like(s["attn"])
+        sets.append(s)
+    ss, ls = w.spatial_shapes, w.level_start
+
+    def step(s):
+        msda.msda_forward(s["value"], ss, ls, s["loc"], s["attn"], out=s["out"])
+        msda.msda_backward(s["value"], ss, ls, s["loc"], s["attn"], s["grad_out"],
+                           grad_value=s["gv"], grad_loc=s["gl"], grad_attn=s["ga"])
+
+    if args.copy_calibration:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for i in range(args.warmup):
+        step(sets[i % args.rotate])
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        s = sets[i % args.rotate]
+        ev[i][0].record(stream)
+        msda.msda_forward(s["value"], ss, ls, s["loc"], s["attn"], out=s["out"])
+        ev[i][1].record(stream)
+        msda.msda_backward(s["value"], ss, ls, s["loc"], s["attn"], s["grad_out"],
+                           grad_value=s["gv"], grad_loc=s["gl"], grad_attn=s["ga"])
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    fwd_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+    bwd_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    value = pts / (ms_per_step * 1e-3)
+
+    def pass_stats(ms, b):
+        t = float(ms.mean()) * 1e-3
+        return {"us_mean": round(t * 1e6, 2), "us_median": round(float(np.median(ms)) * 1e3, 2),
+                "us_p10": round(float(np.percentile(ms, 10)) * 1e3, 2),
+                "us_p90": round(float(np.percentile(ms, 90)) * 1e3, 2),
+                "points_per_s": pts / t, "alg_bytes": b, "alg_GBps": round(b / t / 1e9, 1),
+                "hbm_frac": round(b / t / 1e9 / HBM_PEAK_GBPS, 4)}
+
+    fwd = pass_stats(fwd_ms, b_fwd)
+    bwd = pass_stats(bwd_ms, b_bwd)
+    traffic = measured_traffic()
+    dom, dom_name, dom_b = (bwd, "bwd", b_bwd) if bwd["us_mean"] >= fwd["us_mean"] else (fwd, "fwd", b_fwd)
+    achieved = dom_b / (dom["us_mean"] * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": None if traffic is None or dom_name not in traffic else traffic[dom_name],
+                "kernel": "msda_backward (zero-fill + bwd_kernel)" if dom_name == "bwd" else "fwd_kernel",
+                "alg_bytes_per_launch": dom_b, "alg_bytes_per_point": dom_b / pts}
+
+    result = {
+        "metric": "sampled points/sec (N*Lq*M*L*K), forward + backward",
+        "value": value, "unit": "sampled points/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "encoder-shape fwd+bwd: N=1, levels 100x167/50x84/25x42/13x21, "
+                               "S=Lq=22223, M=8, D=32, K=4, fp32, offsets N(0,2px), softmax weights",
+                   "points_per_step": pts, "buffer_sets_cycled": args.rotate},
+        "roofline": roofline,
+        "fwd": fwd, "bwd": bwd,
+        "kernel_source_sha256": kernel_source_hash(),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,131 @@
+/*
+ * msda.h - C ABI of the multi-scale deformable attention sampling core on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation (page "Deformable DETR", section "Multi-scale deformable
+ * attention", equation MSDeformAttn, the part between the value projection
+ * W'_m and the output projection W_m): for every image n, query q and head m,
+ *
+ *   out[n,q,m,:] = sum_{l<L} sum_{k<K} attn[n,q,m,l,k] *
+ *                  bilinear(value[n, level l, m, :], loc[n,q,m,l,k,:])
+ *
+ * where bilinear() reads the four pixels around a fractional location (same
+ * page, section "Deformable attention module"). Conventions the pages leave
+ * open and this library fixes:
+ *   - loc is normalised: (0,0) and (1,1) are the outer corners of the image,
+ *     loc[...,0] is x (width), loc[...,1] is y (height). The pixel-index
+ *     coordinate is x = fmaf(loc_x, W_l, -0.5f), y = fmaf(loc_y, H_l, -0.5f),
+ *     so pixel j's centre is at (j+0.5)/W_l.
+ *   - zero padding: a corner outside the map reads 0; a sample contributes
+ *     only if -1 <= x < W_l and -1 <= y < H_l (NaN never does).
+ *   - at integer x or y the location gradient is the right-derivative
+ *     (x0 = floor(x) everywhere).
+ *   - pixel (i, j) of level l is row level_start[l] + i*W_l + j of value.
+ *   - attn is applied as given (no softmax, no renormalisation inside).
+ *
+ * Layouts (dense, row-major, as shaped; device arrays aligned to their element
+ * size, loc and grad_loc to 8 bytes since they hold (x, y) pairs):
+ *   value          [N, S, M, D]          dtype         device
+ *   spatial_shapes [L][2] = (H_l, W_l)   int64         HOST, read during the call
+ *   level_start    [L]                   int64         HOST, read during the call
+ *   loc            [N, Lq, M, L, K, 2]   float32       device
+ *   attn           [N, Lq, M, L, K]      float32       device
+ *   out, grad_out  [N, Lq, M, D]         dtype         device
+ *   grad_value     [N, S, M, D]          float32       device
+ *   grad_loc       [N, Lq, M, L, K, 2]   float32       device
+ *   grad_attn      [N, Lq, M, L, K]      float32       device
+ *
+ * Ownership: the caller owns every buffer. The library allocates nothing,
+ * keeps no state and holds no pointer after returning; calls are re-entrant.
+ * Outputs must not alias inputs or each other.
+ *
+ * Asynchrony: work is enqueued on `stream` (0 = the null stream) and the call
+ * returns; nothing synchronises. A fault inside a kernel surfaces at the
+ * caller's next synchronisation.
+ *
+ * Errors: every call returns a status and never aborts, throws or prints.
+ * All argument checks run before any HIP call, so a status other than
+ * MSDA_SUCCESS or MSDA_ERROR_LAUNCH means nothing was enqueued.
+ */
+#ifndef MSDA_H_
+#define MSDA_H_
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum msda_status {
+  MSDA_SUCCESS = 0,
+  MSDA_ERROR_INVALID_VALUE = 1, /* null pointer, negative or zero size, level outside S */
+  MSDA_ERROR_NOT_SUPPORTED = 2, /* L > 16, K > 16, D > 1024, oversized map, unknown dtype */
+  MSDA_ERROR_MISALIGNED = 3,    /* a device pointer not aligned to its element size */
+  MSDA_ERROR_LAUNCH = 4         /* a kernel launch failed (HIP error after enqueue) */
+} msda_status;
+
+typedef enum msda_dtype {
+  MSDA_F32 = 0,  /* value / out / grad_out in float32 */
+  MSDA_BF16 = 1  /* value / out / grad_out in bfloat16; arithmetic in float32 */
+} msda_dtype;
+
+/* Limits of this build. */
+#define MSDA_MAX_LEVELS 16
+#define MSDA_MAX_POINTS 16
+#define MSDA_MAX_CHANNELS 1024
+
+/*
+ * Host-only argument check shared by the entry points (no HIP call, usable
+ * without a GPU). Sizes: N, Lq >= 0 (zero is a no-op); S, M, D, L, K >= 1.
+ * Per level: H_l, W_l >= 1, level_start[l] >= 0 and
+ * level_start[l] + H_l*W_l <= S. Levels need not be contiguous.
+ * Returns MSDA_ERROR_NOT_SUPPORTED for L > 16, K > 16, D > 1024, H_l or W_l
+ * >= 2^24, S*M*D or Lq*M*D above 2^28 - 1 elements, or a dtype other
+ * than MSDA_F32 / MSDA_BF16.
+ */
+msda_status msda_validate(const int64_t *spatial_shapes, const int64_t *level_start,
+                          int64_t N, int64_t S, int64_t M, int64_t D, int64_t L, int64_t Lq,
+                          int64_t K, int dtype);
+
+/*
+ * Forward sampling (page "Deformable DETR", section "Multi-scale deformable
+ * attention", equation MSDeformAttn inside W_m). Writes every element of out
+ * (overwritten, not accumulated). Accumulation is float32 in a fixed order, so
+ * repeated calls give bitwise-identical results. With dtype MSDA_BF16, value
+ * and out are bfloat16: values are widened exactly and the float32 sum is
+ * rounded once to nearest-even on store.
+ */
+msda_status msda_forward(const void *value, const int64_t *spatial_shapes,
+                         const int64_t *level_start, const float *loc, const float *attn,
+                         void *out, int64_t N, int64_t S, int64_t M, int64_t D, int64_t L,
+                         int64_t Lq, int64_t K, int dtype, hipStream_t stream);
+
+/*
+ * Backward of msda_forward: gradients of sum(grad_out * out) with respect to
+ * value, loc and attn (page "Deformable Attention": the bilinear sampling is
+ * differentiable, so gradients reach the sampling offsets; out is linear in
+ * attn and in value).
+ *   grad_attn[n,q,m,l,k] = <grad_out[n,q,m,:], bilinear sample>
+ *   grad_loc [n,q,m,l,k,0] = attn * W_l * <grad_out, d sample / d x>
+ *   grad_loc [n,q,m,l,k,1] = attn * H_l * <grad_out, d sample / d y>
+ *   grad_value[n, corner row, m, :] += attn * corner weight * grad_out
+ * All three outputs are float32 and overwritten (grad_value is zeroed first
+ * on `stream`, also when N*Lq == 0). grad_value is summed with float32
+ * atomics, so its last bits may differ between calls; grad_loc and grad_attn
+ * are deterministic. dtype applies to value and grad_out.
+ */
+msda_status msda_backward(const void *value, const int64_t *spatial_shapes,
+                          const int64_t *level_start, const float *loc, const float *attn,
+                          const void *grad_out, float *grad_value, float *grad_loc,
+                          float *grad_attn, int64_t N, int64_t S, int64_t M, int64_t D,
+                          int64_t L, int64_t Lq, int64_t K, int dtype, hipStream_t stream);
+
+/* Static description of a status code; never NULL. */
+const char *msda_status_string(msda_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSDA_H_ */

@@ -1,0 +1,10 @@
+"""Multi-scale deformable attention sampling core on AMD Instinct MI355X (gfx950).
+
+The forward and backward of the sampling step of MSDeformAttn (page "Deformable
+DETR", section "Multi-scale deformable attention") as hand-written HIP kernels
+behind a C ABI (include/msda.h, libmsda.so). This package holds the kernels'
+sources (csrc/), the in-tree build and the ctypes binding.
+"""
+from .binding import (MSDA_BF16, MSDA_F32, MSDAError, MSDeformAttnSampling,  # noqa: F401
+                      load_library, msda_backward, msda_forward, msda_sample,
+                      msda_status_string, msda_validate)

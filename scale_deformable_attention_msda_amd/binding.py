@@ -1,0 +1,196 @@
+"""ctypes binding of libmsda.so: argument marshalling only.
+
+Every step of the sampling core runs in the HIP kernels behind the C ABI
+(include/msda.h). torch is used for device memory and the current stream; if the
+library is missing or was not built, every call raises instead of computing
+anything elsewhere.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmsda.so")
+
+MSDA_F32 = 0
+MSDA_BF16 = 1
+
+MSDA_SUCCESS = 0
+MSDA_ERROR_INVALID_VALUE = 1
+MSDA_ERROR_NOT_SUPPORTED = 2
+MSDA_ERROR_MISALIGNED = 3
+MSDA_ERROR_LAUNCH = 4
+
+_lib = None
+
+
+class MSDAError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(message)
+        self.status = status
+
+
+def load_library():
+    """Load libmsda.so once and declare its C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it first (__graft_entry__.build(), "
+                           "hipcc --offload-arch=gfx950); there is no fallback path")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, vp, ci = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    lib.msda_validate.argtypes = [vp, vp] + [i64] * 7 + [ci]
+    lib.msda_validate.restype = ci
+    lib.msda_forward.argtypes = [vp] * 6 + [i64] * 7 + [ci, vp]
+    lib.msda_forward.restype = ci
+    lib.msda_backward.argtypes = [vp] * 9 + [i64] * 7 + [ci, vp]
+    lib.msda_backward.restype = ci
+    lib.msda_status_string.argtypes = [ci]
+    lib.msda_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def msda_status_string(status):
+    return load_library().msda_status_string(int(status)).decode()
+
+
+def _raise(status):
+    if status != MSDA_SUCCESS:
+        raise MSDAError(status, msda_status_string(status))
+
+
+def _host_i64(a, shape, what):
+    if isinstance(a, torch.Tensor):
+        if a.device.type != "cpu":
+            raise ValueError(f"{what} must be a host array: the library reads it during the call")
+        a = a.numpy()
+    arr = np.ascontiguousarray(np.asarray(a, dtype=np.int64))
+    if arr.size != int(np.prod(shape)):
+        raise ValueError(f"{what} has {arr.size} entries, expected shape {shape}")
+    return arr.reshape(shape)
+
+
+def _dtype_code(t):
+    if t == torch.float32:
+        return MSDA_F32
+    if t == torch.bfloat16:
+        return MSDA_BF16
+    raise ValueError(f"unsupported dtype {t}: float32 or bfloat16")
+
+
+def _dims(value, loc, attn):
+    if value.dim() != 4 or loc.dim() != 6 or attn.dim() != 5:
+        raise ValueError("expected value [N,S,M,D], loc [N,Lq,M,L,K,2], attn [N,Lq,M,L,K]")
+    N, S, M, D = value.shape
+    N2, Lq, M2, L, K, two = loc.shape
+    if (N2, M2, two) != (N, M, 2) or tuple(attn.shape) != (N, Lq, M, L, K):
+        raise ValueError(f"shape mismatch: value {tuple(value.shape)}, loc {tuple(loc.shape)}, "
+                         f"attn {tuple(attn.shape)}")
+    return N, S, M, D, L, Lq, K
+
+
+def _device_tensor(t, what, dtype=None):
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{what} must be a device tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{what} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+    return t
+
+
+def msda_validate(spatial_shapes, level_start, N, S, M, D, L, Lq, K, dtype=MSDA_F32):
+    """Host-only argument check (no HIP call); returns the status code."""
+    ss = _host_i64(spatial_shapes, (L, 2), "spatial_shapes") if L > 0 else np.zeros((0, 2), np.int64)
+    ls = _host_i64(level_start, (L,), "level_start") if L > 0 else np.zeros((0,), np.int64)
+    return load_library().msda_validate(ss.ctypes.data if L > 0 else None,
+                                        ls.ctypes.data if L > 0 else None,
+                                        N, S, M, D, L, Lq, K, dtype)
+
+
+def msda_forward(value, spatial_shapes, level_start, loc, attn, out=None, stream=None):
+    """out[N,Lq,M,D] (value's dtype) = attention-weighted bilinear samples, per head."""
+    lib = load_library()
+    _device_tensor(value, "value")
+    dt = _dtype_code(value.dtype)
+    _device_tensor(loc, "loc", torch.float32)
+    _device_tensor(attn, "attn", torch.float32)
+    N, S, M, D, L, Lq, K = _dims(value, loc, attn)
+    ss = _host_i64(spatial_shapes, (L, 2), "spatial_shapes")
+    ls = _host_i64(level_start, (L,), "level_start")
+    if out is None:
+        out = torch.empty((N, Lq, M, D), dtype=value.dtype, device=value.device)
+    else:
+        _device_tensor(out, "out", value.dtype)
+        if tuple(out.shape) != (N, Lq, M, D):
+            raise ValueError(f"out must be {(N, Lq, M, D)}")
+    with torch.cuda.device(value.device):
+        s = torch.cuda.current_stream().cuda_stream if stream is None else int(stream)
+        _raise(lib.msda_forward(value.data_ptr(), ss.ctypes.data, ls.ctypes.data, loc.data_ptr(),
+                                attn.data_ptr(), out.data_ptr(), N, S, M, D, L, Lq, K, dt, s))
+    return out
+
+
+def msda_backward(value, spatial_shapes, level_start, loc, attn, grad_out, grad_value=None,
+                  grad_loc=None, grad_attn=None, stream=None):
+    """(grad_value [N,S,M,D], grad_loc [N,Lq,M,L,K,2], grad_attn [N,Lq,M,L,K]), all float32."""
+    lib = load_library()
+    _device_tensor(value, "value")
+    dt = _dtype_code(value.dtype)
+    _device_tensor(loc, "loc", torch.float32)
+    _device_tensor(attn, "attn", torch.float32)
+    _device_tensor(grad_out, "grad_out", value.dtype)
+    N, S, M, D, L, Lq, K = _dims(value, loc, attn)
+    if tuple(grad_out.shape) != (N, Lq, M, D):
+        raise ValueError(f"grad_out must be {(N, Lq, M, D)}")
+    ss = _host_i64(spatial_shapes, (L, 2), "spatial_shapes")
+    ls = _host_i64(level_start, (L,), "level_start")
+    dev = value.device
+    if grad_value is None:
+        grad_value = torch.empty((N, S, M, D), dtype=torch.float32, device=dev)
+    if grad_loc is None:
+        grad_loc = torch.empty((N, Lq, M, L, K, 2), dtype=torch.float32, device=dev)
+    if grad_attn is None:
+        grad_attn = torch.empty((N, Lq, M, L, K), dtype=torch.float32, device=dev)
+    for t, name, shape in ((grad_value, "grad_value", (N, S, M, D)),
+                           (grad_loc, "grad_loc", (N, Lq, M, L, K, 2)),
+                           (grad_attn, "grad_attn", (N, Lq, M, L, K))):
+        _device_tensor(t, name, torch.float32)
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be {shape}")
+    with torch.cuda.device(dev):
+        s = torch.cuda.current_stream().cuda_stream if stream is None else int(stream)
+        _raise(lib.msda_backward(value.data_ptr(), ss.ctypes.data, ls.ctypes.data, loc.data_ptr(),
+                                 attn.data_ptr(), grad_out.data_ptr(), grad_value.data_ptr(),
+                                 grad_loc.data_ptr(), grad_attn.data_ptr(), N, S, M, D, L, Lq, K,
+                                 dt, s))
+    return grad_value, grad_loc, grad_attn
+
+
+class MSDeformAttnSampling(torch.autograd.Function):
+    """Autograd wrapper: forward and backward both run in libmsda.so."""
+
+    @staticmethod
+    def forward(ctx, value, spatial_shapes, level_start, loc, attn):
+        ss = _host_i64(spatial_shapes, (loc.shape[3], 2), "spatial_shapes")
+        ls = _host_i64(level_start, (loc.shape[3],), "level_start")
+        ctx.save_for_backward(value, loc, attn)
+        ctx.levels = (ss, ls)
+        return msda_forward(value, ss, ls, loc, attn)
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        value, loc, attn = ctx.saved_tensors
+        ss, ls = ctx.levels
+        gv, gl, ga = msda_backward(value, ss, ls, loc, attn, grad_out.contiguous())
+        return gv.to(value.dtype), None, None, gl, ga
+
+
+def msda_sample(value, spatial_shapes, level_start, loc, attn):
+    """Differentiable sampling core (value, loc and attn receive gradients)."""
+    return MSDeformAttnSampling.apply(value, spatial_shapes, level_start, loc, attn)

@@ -1,0 +1,152 @@
+// C-ABI layer of the MSDA sampling core: argument checks, batch splitting and
+// kernel dispatch. Every check runs before the first HIP call.
+#include "msda.h"
+
+#include <algorithm>
+
+#include "msda_internal.h"
+
+namespace {
+
+bool mul_ok(int64_t a, int64_t b, int64_t *r) { return !__builtin_mul_overflow(a, b, r); }
+
+bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p) % n) == 0; }
+
+int64_t elem_size(int dtype) { return dtype == MSDA_F32 ? 4 : 2; }
+
+// Images per launch so that the value and grad_out slices of one launch stay
+// below the out-of-bounds sentinel of the kernels.
+int64_t images_per_launch(int64_t S, int64_t M, int64_t D, int64_t Lq) {
+  const int64_t per_image = std::max(S * M * D, Lq * M * D);
+  return std::max<int64_t>(1, msda::kMaxSliceElems / per_image);
+}
+
+msda::Params base_params(const int64_t *spatial_shapes, const int64_t *level_start, int64_t S,
+                         int64_t M, int64_t D, int64_t L, int64_t Lq, int64_t K) {
+  msda::Params p{};
+  p.S = (int32_t)S;
+  p.M = (int32_t)M;
+  p.D = (int32_t)D;
+  p.L = (int32_t)L;
+  p.K = (int32_t)K;
+  p.Lq = (int32_t)Lq;
+  p.LK = (int32_t)(L * K);
+  for (int64_t l = 0; l < L; ++l) {
+    p.lv.H[l] = (int32_t)spatial_shapes[2 * l];
+    p.lv.W[l] = (int32_t)spatial_shapes[2 * l + 1];
+    p.lv.start[l] = (int32_t)level_start[l];
+  }
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+msda_status msda_validate(const int64_t *spatial_shapes, const int64_t *level_start, int64_t N,
+                          int64_t S, int64_t M, int64_t D, int64_t L, int64_t Lq, int64_t K,
+                          int dtype) {
+  if (dtype != MSDA_F32 && dtype != MSDA_BF16) return MSDA_ERROR_NOT_SUPPORTED;
+  if (N < 0 || Lq < 0 || S < 1 || M < 1 || D < 1 || L < 1 || K < 1) return MSDA_ERROR_INVALID_VALUE;
+  if (L > MSDA_MAX_LEVELS || K > MSDA_MAX_POINTS || D > MSDA_MAX_CHANNELS) return MSDA_ERROR_NOT_SUPPORTED;
+  if (spatial_shapes == nullptr || level_start == nullptr) return MSDA_ERROR_INVALID_VALUE;
+  int64_t md, img, qmd;
+  if (!mul_ok(M, D, &md) || !mul_ok(S, md, &img) || !mul_ok(Lq, md, &qmd)) return MSDA_ERROR_NOT_SUPPORTED;
+  if (img > msda::kMaxSliceElems || qmd > msda::kMaxSliceElems) return MSDA_ERROR_NOT_SUPPORTED;
+  for (int64_t l = 0; l < L; ++l) {
+    const int64_t H = spatial_shapes[2 * l], W = spatial_shapes[2 * l + 1], s0 = level_start[l];
+    if (H < 1 || W < 1 || s0 < 0) return MSDA_ERROR_INVALID_VALUE;
+    if (H >= (int64_t(1) << 24) || W >= (int64_t(1) << 24)) return MSDA_ERROR_NOT_SUPPORTED;
+    if (H * W > S || s0 > S - H * W) return MSDA_ERROR_INVALID_VALUE;
+  }
+  // Whole-tensor element counts must fit int64 (they index loc/attn/out).
+  int64_t t;
+  if (!mul_ok(N, img, &t) || !mul_ok(N, qmd, &t)) return MSDA_ERROR_NOT_SUPPORTED;
+  int64_t pts;
+  if (!mul_ok(N, Lq, &pts) || !mul_ok(pts, M * L * K * 2, &t)) return MSDA_ERROR_NOT_SUPPORTED;
+  return MSDA_SUCCESS;
+}
+
+msda_status msda_forward(const void *value, const int64_t *spatial_shapes, const int64_t *level_start,
+                         const float *loc, const float *attn, void *out, int64_t N, int64_t S, int64_t M,
+                         int64_t D, int64_t L, int64_t Lq, int64_t K, int dtype, hipStream_t stream) {
+  msda_status st = msda_validate(spatial_shapes, level_start, N, S, M, D, L, Lq, K, dtype);
+  if (st != MSDA_SUCCESS) return st;
+  if (N == 0 || Lq == 0) return MSDA_SUCCESS;
+  if (!value || !loc || !attn || !out) return MSDA_ERROR_INVALID_VALUE;
+  const int64_t esz = elem_size(dtype);
+  if (!aligned(value, esz) || !aligned(out, esz) || !aligned(loc, 8) || !aligned(attn, 4))
+    return MSDA_ERROR_MISALIGNED;
+
+  const msda::DType dt = dtype == MSDA_F32 ? msda::DType::F32 : msda::DType::BF16;
+  const msda::LaunchShape shape =
+      msda::choose_shape((int)D, dt, reinterpret_cast<uintptr_t>(value) | reinterpret_cast<uintptr_t>(out));
+  msda::Params p = base_params(spatial_shapes, level_start, S, M, D, L, Lq, K);
+  const int64_t step = images_per_launch(S, M, D, Lq);
+  for (int64_t n0 = 0; n0 < N; n0 += step) {
+    const int64_t nb = std::min(step, N - n0);
+    p.N = (int32_t)nb;
+    p.pairs = nb * Lq * M;
+    p.value_elems = (uint32_t)(nb * S * M * D);
+    p.value = static_cast<const char *>(value) + n0 * S * M * D * esz;
+    p.loc = loc + n0 * Lq * M * L * K * 2;
+    p.attn = attn + n0 * Lq * M * L * K;
+    p.out = static_cast<char *>(out) + n0 * Lq * M * D * esz;
+    if (msda::launch_forward(p, dt, shape, stream) != hipSuccess) return MSDA_ERROR_LAUNCH;
+  }
+  return MSDA_SUCCESS;
+}
+
+msda_status msda_backward(const void *value, const int64_t *spatial_shapes, const int64_t *level_start,
+                          const float *loc, const float *attn, const void *grad_out, float *grad_value,
+                          float *grad_loc, float *grad_attn, int64_t N, int64_t S, int64_t M, int64_t D,
+                          int64_t L, int64_t Lq, int64_t K, int dtype, hipStream_t stream) {
+  msda_status st = msda_validate(spatial_shapes, level_start, N, S, M, D, L, Lq, K, dtype);
+  if (st != MSDA_SUCCESS) return st;
+  if (N == 0) return MSDA_SUCCESS;
+  if (!grad_value) return MSDA_ERROR_INVALID_VALUE;
+  if (!aligned(grad_value, 4)) return MSDA_ERROR_MISALIGNED;
+  const int64_t esz = elem_size(dtype);
+  if (Lq > 0) {
+    if (!value || !loc || !attn || !grad_out || !grad_loc || !grad_attn) return MSDA_ERROR_INVALID_VALUE;
+    if (!aligned(value, esz) || !aligned(grad_out, esz) || !aligned(loc, 8) || !aligned(attn, 4) ||
+        !aligned(grad_loc, 8) || !aligned(grad_attn, 4))
+      return MSDA_ERROR_MISALIGNED;
+  }
+  if (msda::launch_zero(grad_value, N * S * M * D, stream) != hipSuccess) return MSDA_ERROR_LAUNCH;
+  if (Lq == 0) return MSDA_SUCCESS;
+
+  const msda::DType dt = dtype == MSDA_F32 ? msda::DType::F32 : msda::DType::BF16;
+  const msda::LaunchShape shape = msda::choose_shape(
+      (int)D, dt, reinterpret_cast<uintptr_t>(value) | reinterpret_cast<uintptr_t>(grad_out));
+  msda::Params p = base_params(spatial_shapes, level_start, S, M, D, L, Lq, K);
+  const int64_t step = images_per_launch(S, M, D, Lq);
+  for (int64_t n0 = 0; n0 < N; n0 += step) {
+    const int64_t nb = std::min(step, N - n0);
+    p.N = (int32_t)nb;
+    p.pairs = nb * Lq * M;
+    p.value_elems = (uint32_t)(nb * S * M * D);
+    p.value = static_cast<const char *>(value) + n0 * S * M * D * esz;
+    p.loc = loc + n0 * Lq * M * L * K * 2;
+    p.attn = attn + n0 * Lq * M * L * K;
+    p.grad_out = static_cast<const char *>(grad_out) + n0 * Lq * M * D * esz;
+    p.grad_value = grad_value + n0 * S * M * D;
+    p.grad_loc = grad_loc + n0 * Lq * M * L * K * 2;
+    p.grad_attn = grad_attn + n0 * Lq * M * L * K;
+    if (msda::launch_backward(p, dt, shape, stream) != hipSuccess) return MSDA_ERROR_LAUNCH;
+  }
+  return MSDA_SUCCESS;
+}
+
+const char *msda_status_string(msda_status status) {
+  switch (status) {
+    case MSDA_SUCCESS: return "MSDA_SUCCESS: no error";
+    case MSDA_ERROR_INVALID_VALUE: return "MSDA_ERROR_INVALID_VALUE: null pointer, bad size or level outside S";
+    case MSDA_ERROR_NOT_SUPPORTED: return "MSDA_ERROR_NOT_SUPPORTED: shape, size or dtype beyond this build's limits";
+    case MSDA_ERROR_MISALIGNED: return "MSDA_ERROR_MISALIGNED: a device pointer is not aligned to its element size";
+    case MSDA_ERROR_LAUNCH: return "MSDA_ERROR_LAUNCH: a kernel launch failed";
+  }
+  return "MSDA: unknown status";
+}
+
+}  // extern "C"

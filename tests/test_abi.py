@@ -1,0 +1,133 @@
+"""The C-ABI library on the host (no GPU needed): it loads, exports every symbol
+the header declares, and rejects bad arguments before making any HIP call."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import scale_deformable_attention_msda_amd as msda
+from scale_deformable_attention_msda_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msda.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(binding.LIB_PATH),
+                                reason="libmsda.so not built (run __graft_entry__.build())")
+
+COCO = np.array([[100, 167], [50, 84], [25, 42], [13, 21]], dtype=np.int64)
+STARTS = np.array([0, 16700, 20900, 21950], dtype=np.int64)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(msda_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["msda_backward", "msda_forward", "msda_status_string",
+                                    "msda_validate"]
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(binding.LIB_PATH)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    for code in range(5):
+        s = msda.msda_status_string(code)
+        assert s.startswith("MSDA_")
+    assert "unknown" in msda.msda_status_string(99)
+
+
+def v(*args, **kw):
+    return msda.msda_validate(*args, **kw)
+
+
+def test_validate_accepts_the_workload_shapes():
+    assert v(COCO, STARTS, 1, 22223, 8, 32, 4, 22223, 4) == 0
+    assert v(COCO, STARTS, 8, 22223, 8, 32, 4, 22223, 4, dtype=1) == 0
+    assert v(COCO, STARTS, 2, 22223, 8, 32, 4, 300, 8) == 0
+    assert v(COCO, STARTS, 0, 22223, 8, 32, 4, 0, 4) == 0  # empty batch is a no-op
+
+
+@pytest.mark.parametrize("args,code", [
+    ((1, 22223, 8, 32, 4, 100, 4, 2), 2),        # unknown dtype
+    ((-1, 22223, 8, 32, 4, 100, 4, 0), 1),       # negative N
+    ((1, 22223, 8, 32, 4, -3, 4, 0), 1),         # negative Lq
+    ((1, 22223, 0, 32, 4, 100, 4, 0), 1),        # M = 0
+    ((1, 22223, 8, 0, 4, 100, 4, 0), 1),         # D = 0
+    ((1, 22223, 8, 32, 4, 100, 0, 0), 1),        # K = 0
+    ((1, 22223, 8, 32, 4, 100, 17, 0), 2),       # K > 16
+    ((1, 22223, 8, 1025, 4, 100, 4, 0), 2),      # D > 1024
+    ((1, 22222, 8, 32, 4, 100, 4, 0), 1),        # last level runs past S
+    ((1, 22223, 16, 1024, 4, 100, 4, 0), 2),     # S*M*D beyond the per-image limit
+])
+def test_validate_rejects(args, code):
+    N, S, M, D, L, Lq, K, dt = args
+    assert v(COCO, STARTS, N, S, M, D, L, Lq, K, dtype=dt) == code
+
+
+def test_validate_level_geometry():
+    lib = binding.load_library()
+    ss = np.array([[4, 4], [0, 3]], dtype=np.int64)
+    ls = np.array([0, 16], dtype=np.int64)
+    assert lib.msda_validate(ss.ctypes.data, ls.ctypes.data, 1, 40, 1, 1, 2, 1, 1, 0) == 1  # H = 0
+    ss = np.array([[4, 4], [2, 3]], dtype=np.int64)
+    ls = np.array([0, -1], dtype=np.int64)
+    assert lib.msda_validate(ss.ctypes.data, ls.ctypes.data, 1, 40, 1, 1, 2, 1, 1, 0) == 1  # start < 0
+    ls = np.array([0, 16], dtype=np.int64)
+    assert lib.msda_validate(ss.ctypes.data, ls.ctypes.data, 1, 22, 1, 1, 2, 1, 1, 0) == 0
+    assert lib.msda_validate(ss.ctypes.data, ls.ctypes.data, 1, 21, 1, 1, 2, 1, 1, 0) == 1
+    ss17 = np.ones((17, 2), dtype=np.int64)
+    ls17 = np.arange(17, dtype=np.int64)
+    assert lib.msda_validate(ss17.ctypes.data, ls17.ctypes.data, 1, 17, 1, 1, 17, 1, 1, 0) == 2
+    ssbig = np.array([[1, 1 << 24]], dtype=np.int64)
+    assert lib.msda_validate(ssbig.ctypes.data, np.zeros(1, np.int64).ctypes.data,
+                             1, 1 << 24, 1, 1, 1, 1, 1, 0) == 2
+    assert lib.msda_validate(None, None, 1, 4, 1, 1, 1, 1, 1, 0) == 1  # null host tables
+
+
+def test_entry_points_reject_bad_pointers_before_any_hip_call():
+    lib = binding.load_library()
+    ss = COCO.ctypes.data
+    ls = STARTS.ctypes.data
+    dims = (1, 22223, 8, 32, 4, 22223, 4)
+    A = 0x10000  # never dereferenced: every call below fails its checks first
+    # null device pointers
+    assert lib.msda_forward(None, ss, ls, A, A, A, *dims, 0, None) == 1
+    assert lib.msda_forward(A, ss, ls, A, A, None, *dims, 0, None) == 1
+    assert lib.msda_backward(A, ss, ls, A, A, A, None, A, A, *dims, 0, None) == 1
+    assert lib.msda_backward(A, ss, ls, A, A, None, A, A, A, *dims, 0, None) == 1
+    # misaligned: loc must be 8-byte aligned, fp32 arrays 4-byte, bf16 2-byte
+    assert lib.msda_forward(A, ss, ls, A + 4, A, A, *dims, 0, None) == 3
+    assert lib.msda_forward(A + 2, ss, ls, A, A, A, *dims, 0, None) == 3
+    assert lib.msda_forward(A + 1, ss, ls, A, A, A, *dims, 1, None) == 3
+    assert lib.msda_backward(A, ss, ls, A, A, A, A + 2, A, A, *dims, 0, None) == 3
+    assert lib.msda_backward(A, ss, ls, A, A, A, A, A + 4, A, *dims, 0, None) == 3
+    # invalid shapes reach no pointer at all
+    assert lib.msda_forward(A, ss, ls, A, A, A, 1, 22223, 8, 32, 4, 22223, 17, 0, None) == 2
+    assert lib.msda_backward(A, ss, ls, A, A, A, A, A, A, 1, 22223, 8, 32, 4, 22223, 4, 5, None) == 2
+    # an empty problem is a successful no-op without touching memory
+    assert lib.msda_forward(None, ss, ls, None, None, None, 0, 22223, 8, 32, 4, 10, 4, 0, None) == 0
+    assert lib.msda_forward(None, ss, ls, None, None, None, 1, 22223, 8, 32, 4, 0, 4, 0, None) == 0
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch):
+    monkeypatch.setattr(binding, "_lib", None)
+    monkeypatch.setattr(binding, "LIB_PATH", binding.LIB_PATH + ".absent")
+    with pytest.raises(RuntimeError, match="missing"):
+        binding.load_library()
+
+
+def test_binding_rejects_host_tensors():
+    torch = pytest.importorskip("torch")
+    x = torch.zeros(1, 4, 1, 1)
+    loc = torch.zeros(1, 1, 1, 1, 1, 2)
+    attn = torch.zeros(1, 1, 1, 1, 1)
+    with pytest.raises(ValueError, match="device tensor"):
+        msda.msda_forward(x, [[2, 2]], [0], loc, attn)
