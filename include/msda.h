@@ -50,6 +50,7 @@
 #ifndef MSDA_H_
 #define MSDA_H_
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -62,7 +63,8 @@ typedef enum msda_status {
   MSDA_ERROR_INVALID_VALUE = 1, /* null pointer, negative or zero size, level outside S */
   MSDA_ERROR_NOT_SUPPORTED = 2, /* L > 16, K > 16, D > 1024, oversized map, unknown dtype */
   MSDA_ERROR_MISALIGNED = 3,    /* a device pointer not aligned to its element size */
-  MSDA_ERROR_LAUNCH = 4         /* a kernel launch failed (HIP error after enqueue) */
+  MSDA_ERROR_LAUNCH = 4,        /* a kernel launch failed (HIP error after enqueue) */
+  MSDA_ERROR_WORKSPACE = 5      /* backward workspace missing or too small */
 } msda_status;
 
 typedef enum msda_dtype {
@@ -79,10 +81,11 @@ typedef enum msda_dtype {
  * Host-only argument check shared by the entry points (no HIP call, usable
  * without a GPU). Sizes: N, Lq >= 0 (zero is a no-op); S, M, D, L, K >= 1.
  * Per level: H_l, W_l >= 1, level_start[l] >= 0 and
- * level_start[l] + H_l*W_l <= S. Levels need not be contiguous.
+ * level_start[l] + H_l*W_l <= S; the levels' row ranges must not overlap
+ * (MSDA_ERROR_INVALID_VALUE otherwise) but may leave gaps.
  * Returns MSDA_ERROR_NOT_SUPPORTED for L > 16, K > 16, D > 1024, H_l or W_l
- * >= 2^24, S*M*D or Lq*M*D above 2^28 - 1 elements, or a dtype other
- * than MSDA_F32 / MSDA_BF16.
+ * >= 2^24, S*M*D or Lq*M*D above 2^28 - 1 elements, Lq*M*L*K above 2^29,
+ * or a dtype other than MSDA_F32 / MSDA_BF16.
  */
 msda_status msda_validate(const int64_t *spatial_shapes, const int64_t *level_start,
                           int64_t N, int64_t S, int64_t M, int64_t D, int64_t L, int64_t Lq,
@@ -102,6 +105,16 @@ msda_status msda_forward(const void *value, const int64_t *spatial_shapes,
                          int64_t Lq, int64_t K, int dtype, hipStream_t stream);
 
 /*
+ * Bytes of device workspace msda_backward needs for these sizes (the same
+ * checks as msda_validate apply). The workspace holds a counting sort of the
+ * samples by the 8x8-pixel tile of the value map they touch: a few counters
+ * per tile plus four 32-bit entries per sample, about 16*N*Lq*M*L*K bytes.
+ */
+msda_status msda_backward_workspace_size(const int64_t *spatial_shapes, const int64_t *level_start,
+                                         int64_t N, int64_t S, int64_t M, int64_t D, int64_t L,
+                                         int64_t Lq, int64_t K, int dtype, size_t *bytes);
+
+/*
  * Backward of msda_forward: gradients of sum(grad_out * out) with respect to
  * value, loc and attn (page "Deformable Attention": the bilinear sampling is
  * differentiable, so gradients reach the sampling offsets; out is linear in
@@ -110,16 +123,21 @@ msda_status msda_forward(const void *value, const int64_t *spatial_shapes,
  *   grad_loc [n,q,m,l,k,0] = attn * W_l * <grad_out, d sample / d x>
  *   grad_loc [n,q,m,l,k,1] = attn * H_l * <grad_out, d sample / d y>
  *   grad_value[n, corner row, m, :] += attn * corner weight * grad_out
- * All three outputs are float32 and overwritten (grad_value is zeroed first
- * on `stream`, also when N*Lq == 0). grad_value is summed with float32
- * atomics, so its last bits may differ between calls; grad_loc and grad_attn
- * are deterministic. dtype applies to value and grad_out.
+ * All three outputs are float32 and overwritten (every grad_value row is
+ * written, including rows no sample touches). dtype applies to value and
+ * grad_out. `workspace` is device memory of at least the size
+ * msda_backward_workspace_size reports, 256-byte aligned, owned by the caller
+ * and used only while the enqueued work runs (calls that overlap on different
+ * streams need separate workspaces); MSDA_ERROR_WORKSPACE if it is missing or
+ * too small. grad_loc and grad_attn are deterministic; grad_value sums each
+ * pixel's contributions in float32 in an order that can vary between calls.
  */
 msda_status msda_backward(const void *value, const int64_t *spatial_shapes,
                           const int64_t *level_start, const float *loc, const float *attn,
                           const void *grad_out, float *grad_value, float *grad_loc,
                           float *grad_attn, int64_t N, int64_t S, int64_t M, int64_t D,
-                          int64_t L, int64_t Lq, int64_t K, int dtype, hipStream_t stream);
+                          int64_t L, int64_t Lq, int64_t K, int dtype, void *workspace,
+                          size_t workspace_bytes, hipStream_t stream);
 
 /* Static description of a status code; never NULL. */
 const char *msda_status_string(msda_status status);

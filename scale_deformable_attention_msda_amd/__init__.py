@@ -6,5 +6,6 @@ behind a C ABI (include/msda.h, libmsda.so). This package holds the kernels'
 sources (csrc/), the in-tree build and the ctypes binding.
 """
 from .binding import (MSDA_BF16, MSDA_F32, MSDAError, MSDeformAttnSampling,  # noqa: F401
-                      load_library, msda_backward, msda_forward, msda_sample,
+                      load_library, msda_backward, msda_backward_workspace_size,
+                      msda_forward, msda_sample,
                       msda_status_string, msda_validate)

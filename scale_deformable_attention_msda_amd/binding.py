@@ -23,6 +23,7 @@ MSDA_ERROR_INVALID_VALUE = 1
 MSDA_ERROR_NOT_SUPPORTED = 2
 MSDA_ERROR_MISALIGNED = 3
 MSDA_ERROR_LAUNCH = 4
+MSDA_ERROR_WORKSPACE = 5
 
 _lib = None
 
@@ -47,8 +48,10 @@ def load_library():
     lib.msda_validate.restype = ci
     lib.msda_forward.argtypes = [vp] * 6 + [i64] * 7 + [ci, vp]
     lib.msda_forward.restype = ci
-    lib.msda_backward.argtypes = [vp] * 9 + [i64] * 7 + [ci, vp]
+    lib.msda_backward.argtypes = [vp] * 9 + [i64] * 7 + [ci, vp, ctypes.c_size_t, vp]
     lib.msda_backward.restype = ci
+    lib.msda_backward_workspace_size.argtypes = [vp, vp] + [i64] * 7 + [ci, ctypes.POINTER(ctypes.c_size_t)]
+    lib.msda_backward_workspace_size.restype = ci
     lib.msda_status_string.argtypes = [ci]
     lib.msda_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -136,9 +139,23 @@ def msda_forward(value, spatial_shapes, level_start, loc, attn, out=None, stream
     return out
 
 
+def msda_backward_workspace_size(spatial_shapes, level_start, N, S, M, D, L, Lq, K, dtype=MSDA_F32):
+    """Bytes of device workspace msda_backward needs for these sizes."""
+    ss = _host_i64(spatial_shapes, (L, 2), "spatial_shapes")
+    ls = _host_i64(level_start, (L,), "level_start")
+    out = ctypes.c_size_t(0)
+    _raise(load_library().msda_backward_workspace_size(ss.ctypes.data, ls.ctypes.data, N, S, M, D, L, Lq,
+                                                       K, dtype, ctypes.byref(out)))
+    return out.value
+
+
 def msda_backward(value, spatial_shapes, level_start, loc, attn, grad_out, grad_value=None,
-                  grad_loc=None, grad_attn=None, stream=None):
-    """(grad_value [N,S,M,D], grad_loc [N,Lq,M,L,K,2], grad_attn [N,Lq,M,L,K]), all float32."""
+                  grad_loc=None, grad_attn=None, workspace=None, stream=None):
+    """(grad_value [N,S,M,D], grad_loc [N,Lq,M,L,K,2], grad_attn [N,Lq,M,L,K]), all float32.
+
+    ``workspace``: optional uint8 device tensor of at least
+    msda_backward_workspace_size bytes; allocated from torch's caching
+    allocator when omitted."""
     lib = load_library()
     _device_tensor(value, "value")
     dt = _dtype_code(value.dtype)
@@ -163,12 +180,17 @@ def msda_backward(value, spatial_shapes, level_start, loc, attn, grad_out, grad_
         _device_tensor(t, name, torch.float32)
         if tuple(t.shape) != shape:
             raise ValueError(f"{name} must be {shape}")
+    need = msda_backward_workspace_size(ss, ls, N, S, M, D, L, Lq, K, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    else:
+        _device_tensor(workspace, "workspace", torch.uint8)
     with torch.cuda.device(dev):
         s = torch.cuda.current_stream().cuda_stream if stream is None else int(stream)
         _raise(lib.msda_backward(value.data_ptr(), ss.ctypes.data, ls.ctypes.data, loc.data_ptr(),
                                  attn.data_ptr(), grad_out.data_ptr(), grad_value.data_ptr(),
                                  grad_loc.data_ptr(), grad_attn.data_ptr(), N, S, M, D, L, Lq, K,
-                                 dt, s))
+                                 dt, workspace.data_ptr(), workspace.numel(), s))
     return grad_value, grad_loc, grad_attn
 
 

@@ -15,10 +15,14 @@ bool aligned(const void *p, uintptr_t n) { return (reinterpret_cast<uintptr_t>(p
 int64_t elem_size(int dtype) { return dtype == MSDA_F32 ? 4 : 2; }
 
 // Images per launch so that the value and grad_out slices of one launch stay
-// below the out-of-bounds sentinel of the kernels.
-int64_t images_per_launch(int64_t S, int64_t M, int64_t D, int64_t Lq) {
+// below the out-of-bounds sentinel of the kernels and its samples keep 32-bit
+// indices (with four tile entries per sample).
+int64_t images_per_launch(int64_t S, int64_t M, int64_t D, int64_t Lq, int64_t L, int64_t K) {
   const int64_t per_image = std::max(S * M * D, Lq * M * D);
-  return std::max<int64_t>(1, msda::kMaxSliceElems / per_image);
+  int64_t n = std::max<int64_t>(1, msda::kMaxSliceElems / per_image);
+  const int64_t samples = std::max<int64_t>(1, Lq * M * L * K);
+  n = std::min(n, std::max<int64_t>(1, (msda::kMaxSliceSamples / 4) / samples));
+  return n;
 }
 
 msda::Params base_params(const int64_t *spatial_shapes, const int64_t *level_start, int64_t S,
@@ -36,7 +40,14 @@ msda::Params base_params(const int64_t *spatial_shapes, const int64_t *level_sta
     p.lv.W[l] = (int32_t)spatial_shapes[2 * l + 1];
     p.lv.start[l] = (int32_t)level_start[l];
   }
+  msda::fill_tiles(p.lv, spatial_shapes, L, &p.TPI);
   return p;
+}
+
+bool levels_cover_all_rows(const int64_t *spatial_shapes, int64_t L, int64_t S) {
+  int64_t covered = 0;
+  for (int64_t l = 0; l < L; ++l) covered += spatial_shapes[2 * l] * spatial_shapes[2 * l + 1];
+  return covered == S;  // levels are disjoint (checked), so this means no gap
 }
 
 }  // namespace
@@ -59,11 +70,21 @@ msda_status msda_validate(const int64_t *spatial_shapes, const int64_t *level_st
     if (H >= (int64_t(1) << 24) || W >= (int64_t(1) << 24)) return MSDA_ERROR_NOT_SUPPORTED;
     if (H * W > S || s0 > S - H * W) return MSDA_ERROR_INVALID_VALUE;
   }
+  // Levels occupy disjoint row ranges of value (each row belongs to at most
+  // one level, so every grad_value row has one owner).
+  for (int64_t a = 0; a < L; ++a)
+    for (int64_t b = a + 1; b < L; ++b) {
+      const int64_t a0 = level_start[a], a1 = a0 + spatial_shapes[2 * a] * spatial_shapes[2 * a + 1];
+      const int64_t b0 = level_start[b], b1 = b0 + spatial_shapes[2 * b] * spatial_shapes[2 * b + 1];
+      if (a0 < b1 && b0 < a1) return MSDA_ERROR_INVALID_VALUE;
+    }
   // Whole-tensor element counts must fit int64 (they index loc/attn/out).
   int64_t t;
   if (!mul_ok(N, img, &t) || !mul_ok(N, qmd, &t)) return MSDA_ERROR_NOT_SUPPORTED;
   int64_t pts;
   if (!mul_ok(N, Lq, &pts) || !mul_ok(pts, M * L * K * 2, &t)) return MSDA_ERROR_NOT_SUPPORTED;
+  // One image's samples need 32-bit indices in the backward's tile entries.
+  if (Lq * M * L * K > msda::kMaxSliceSamples / 4) return MSDA_ERROR_NOT_SUPPORTED;
   return MSDA_SUCCESS;
 }
 
@@ -82,7 +103,7 @@ msda_status msda_forward(const void *value, const int64_t *spatial_shapes, const
   const msda::LaunchShape shape =
       msda::choose_shape((int)D, dt, reinterpret_cast<uintptr_t>(value) | reinterpret_cast<uintptr_t>(out));
   msda::Params p = base_params(spatial_shapes, level_start, S, M, D, L, Lq, K);
-  const int64_t step = images_per_launch(S, M, D, Lq);
+  const int64_t step = images_per_launch(S, M, D, Lq, L, K);
   for (int64_t n0 = 0; n0 < N; n0 += step) {
     const int64_t nb = std::min(step, N - n0);
     p.N = (int32_t)nb;
@@ -97,34 +118,62 @@ msda_status msda_forward(const void *value, const int64_t *spatial_shapes, const
   return MSDA_SUCCESS;
 }
 
+msda_status msda_backward_workspace_size(const int64_t *spatial_shapes, const int64_t *level_start, int64_t N,
+                                         int64_t S, int64_t M, int64_t D, int64_t L, int64_t Lq, int64_t K,
+                                         int dtype, size_t *bytes) {
+  if (!bytes) return MSDA_ERROR_INVALID_VALUE;
+  msda_status st = msda_validate(spatial_shapes, level_start, N, S, M, D, L, Lq, K, dtype);
+  if (st != MSDA_SUCCESS) return st;
+  const int64_t step = std::min(std::max<int64_t>(N, 1), images_per_launch(S, M, D, Lq, L, K));
+  *bytes = msda::workspace_layout(spatial_shapes, L, step, M, Lq, K).bytes;
+  return MSDA_SUCCESS;
+}
+
 msda_status msda_backward(const void *value, const int64_t *spatial_shapes, const int64_t *level_start,
                           const float *loc, const float *attn, const void *grad_out, float *grad_value,
                           float *grad_loc, float *grad_attn, int64_t N, int64_t S, int64_t M, int64_t D,
-                          int64_t L, int64_t Lq, int64_t K, int dtype, hipStream_t stream) {
+                          int64_t L, int64_t Lq, int64_t K, int dtype, void *workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
   msda_status st = msda_validate(spatial_shapes, level_start, N, S, M, D, L, Lq, K, dtype);
   if (st != MSDA_SUCCESS) return st;
   if (N == 0) return MSDA_SUCCESS;
   if (!grad_value) return MSDA_ERROR_INVALID_VALUE;
   if (!aligned(grad_value, 4)) return MSDA_ERROR_MISALIGNED;
   const int64_t esz = elem_size(dtype);
+  const int64_t step = images_per_launch(S, M, D, Lq, L, K);
+  const msda::WorkspaceLayout wl = msda::workspace_layout(spatial_shapes, L, std::min(step, N), M, Lq, K);
   if (Lq > 0) {
     if (!value || !loc || !attn || !grad_out || !grad_loc || !grad_attn) return MSDA_ERROR_INVALID_VALUE;
     if (!aligned(value, esz) || !aligned(grad_out, esz) || !aligned(loc, 8) || !aligned(attn, 4) ||
         !aligned(grad_loc, 8) || !aligned(grad_attn, 4))
       return MSDA_ERROR_MISALIGNED;
+    if (!workspace || workspace_bytes < wl.bytes) return MSDA_ERROR_WORKSPACE;
+    if (!aligned(workspace, 256)) return MSDA_ERROR_MISALIGNED;
   }
-  if (msda::launch_zero(grad_value, N * S * M * D, stream) != hipSuccess) return MSDA_ERROR_LAUNCH;
+  // Rows outside every level (or every row when there are no queries) get
+  // no tile owner: zero them in full first.
+  if (Lq == 0 || !levels_cover_all_rows(spatial_shapes, L, S)) {
+    if (msda::launch_zero(grad_value, N * S * M * D, stream) != hipSuccess) return MSDA_ERROR_LAUNCH;
+  }
   if (Lq == 0) return MSDA_SUCCESS;
 
   const msda::DType dt = dtype == MSDA_F32 ? msda::DType::F32 : msda::DType::BF16;
   const msda::LaunchShape shape = msda::choose_shape(
       (int)D, dt, reinterpret_cast<uintptr_t>(value) | reinterpret_cast<uintptr_t>(grad_out));
   msda::Params p = base_params(spatial_shapes, level_start, S, M, D, L, Lq, K);
-  const int64_t step = images_per_launch(S, M, D, Lq);
+  char *ws = static_cast<char *>(workspace);
+  p.ws.tile_count = reinterpret_cast<uint32_t *>(ws + wl.off_count);
+  p.ws.tile_cursor = reinterpret_cast<uint32_t *>(ws + wl.off_cursor);
+  p.ws.tile_start = reinterpret_cast<uint32_t *>(ws + wl.off_start);
+  p.ws.work_tile = reinterpret_cast<uint32_t *>(ws + wl.off_wtile);
+  p.ws.work_part = reinterpret_cast<uint32_t *>(ws + wl.off_wpart);
+  p.ws.n_work = reinterpret_cast<uint32_t *>(ws + wl.off_nwork);
+  p.ws.entries = reinterpret_cast<uint32_t *>(ws + wl.off_entries);
   for (int64_t n0 = 0; n0 < N; n0 += step) {
     const int64_t nb = std::min(step, N - n0);
     p.N = (int32_t)nb;
     p.pairs = nb * Lq * M;
+    p.T = (int32_t)(nb * M * p.TPI);
     p.value_elems = (uint32_t)(nb * S * M * D);
     p.value = static_cast<const char *>(value) + n0 * S * M * D * esz;
     p.loc = loc + n0 * Lq * M * L * K * 2;
@@ -145,6 +194,7 @@ const char *msda_status_string(msda_status status) {
     case MSDA_ERROR_NOT_SUPPORTED: return "MSDA_ERROR_NOT_SUPPORTED: shape, size or dtype beyond this build's limits";
     case MSDA_ERROR_MISALIGNED: return "MSDA_ERROR_MISALIGNED: a device pointer is not aligned to its element size";
     case MSDA_ERROR_LAUNCH: return "MSDA_ERROR_LAUNCH: a kernel launch failed";
+    case MSDA_ERROR_WORKSPACE: return "MSDA_ERROR_WORKSPACE: workspace missing or smaller than msda_backward_workspace_size";
   }
   return "MSDA: unknown status";
 }

@@ -2,6 +2,7 @@
 // gfx950 kernels (msda_kernels.hip). Not part of the public ABI.
 #pragma once
 
+#include <stddef.h>
 #include <stdint.h>
 #include <hip/hip_runtime_api.h>
 
@@ -17,11 +18,37 @@ constexpr int kBlock = 256;  // threads per workgroup: four wave64s
 // added together (corner + idle lane), times 4 bytes, still fit in 32 bits.
 constexpr uint32_t kOobElem = 1u << 28;
 constexpr int64_t kMaxSliceElems = (int64_t)kOobElem - 1;
+// Samples (N*Lq*M*L*K) of one launch must have 32-bit indices.
+constexpr int64_t kMaxSliceSamples = (int64_t)1 << 31;
+
+// grad_value is produced per 8x8-pixel tile of each (image, head, level).
+constexpr int kTile = 8;
+constexpr int kTilePix = kTile * kTile;
+// Entries (sample, tile) handled by one workgroup of the grad_value pass; a
+// tile with more entries is split into several work items whose partial sums
+// are combined with float atomics.
+constexpr int kPartEntries = 4096;
+// Channels handled by one grad_value work item.
+constexpr int kChanGroup = 64;
 
 struct LevelTable {
   int32_t H[kMaxLevels];
   int32_t W[kMaxLevels];
   int32_t start[kMaxLevels];
+  int32_t TH[kMaxLevels];    // tile rows of the level
+  int32_t TW[kMaxLevels];    // tile columns of the level
+  int32_t toff[kMaxLevels];  // first tile of the level within one (image, head)
+};
+
+// Backward scratch, carved out of the caller's workspace.
+struct Workspace {
+  uint32_t *tile_count;   // [T]   entries per tile
+  uint32_t *tile_cursor;  // [T]   fill cursor of the scatter pass
+  uint32_t *tile_start;   // [T+1] first entry of each tile
+  uint32_t *work_tile;    // [Wmax] work items of the grad_value pass
+  uint32_t *work_part;    // [Wmax]
+  uint32_t *n_work;       // [1]
+  uint32_t *entries;      // [Emax] sample index of each (sample, tile) entry, tile-major
 };
 
 // One launch covers images [0, N) of the pointers below (the host offsets the
@@ -40,6 +67,10 @@ struct Params {
   int32_t lpp;           // lanes per (n, q, m) pair, a power of two <= 64
   int32_t pc;            // points per descriptor chunk
   uint32_t value_elems;  // elements of value in this launch (< kOobElem)
+  int32_t TPI;           // tiles per (image, head) over all levels
+  int32_t T;             // tiles of the launch: N * M * TPI
+  int32_t qpb;           // queries per workgroup of the binning passes
+  Workspace ws;
   LevelTable lv;
 };
 
@@ -53,6 +84,15 @@ struct LaunchShape {
 
 // Picks the lane mapping for a channel count, element type and pointer alignment.
 LaunchShape choose_shape(int D, DType dt, uintptr_t align_bits);
+
+// Tile table and workspace layout of a launch covering `nimg` images.
+struct WorkspaceLayout {
+  int64_t T, Wmax, Emax;
+  size_t off_count, off_cursor, off_start, off_wtile, off_wpart, off_nwork, off_entries, bytes;
+};
+WorkspaceLayout workspace_layout(const int64_t *spatial_shapes, int64_t L, int64_t nimg, int64_t M,
+                                 int64_t Lq, int64_t K);
+void fill_tiles(LevelTable &lv, const int64_t *spatial_shapes, int64_t L, int32_t *TPI);
 
 hipError_t launch_forward(const Params &p, DType dt, const LaunchShape &s, hipStream_t stream);
 hipError_t launch_backward(const Params &p, DType dt, const LaunchShape &s, hipStream_t stream);

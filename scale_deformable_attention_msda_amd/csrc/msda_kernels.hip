@@ -22,9 +22,9 @@
 //   * Workgroups are renumbered so that each XCD (own L2) works on one
 //     contiguous range of queries, which sample overlapping value rows.
 //   * Backward: per sample, the three dot products (grad_attn and the two
-//     location gradients) are reduced across the pair's lanes with DPP; the
-//     results are staged in LDS and written coalesced. grad_value receives
-//     fp32 buffer atomics.
+//     location gradients) are reduced across the pair's lanes with DPP and
+//     written coalesced; grad_value is built per pixel tile from a counting
+//     sort of the samples (see the backward section).
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
@@ -285,16 +285,31 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(const Params p) {
 }
 
 // --------------------------------------------------------------- backward
+//
+// The backward runs as a short pipeline on the caller's stream:
+//   1. bwd_sample_kernel: grad_attn and grad_loc. Same gather as the forward;
+//      the three dot products of a sample are reduced across the pair's lanes.
+//   2. bin_kernel<count> / scan_kernel / bin_kernel<scatter>: a counting sort
+//      of (sample, 8x8-pixel tile) entries, one entry per tile that a sample's
+//      in-map corners touch. Workgroups own one (image, head) and a range of
+//      queries, so their tile histogram fits in LDS and only nonzero bins reach
+//      global memory (integer atomics, a few per workgroup).
+//   3. gv_kernel: one workgroup per tile (or per slice of a crowded tile). Its
+//      entries' corner contributions are bucketed by pixel in LDS, then each
+//      thread sums the contributions to the pixel it owns in registers and
+//      stores them. Float atomics appear only where a crowded tile is split.
+// gfx950 float atomics (global and LDS) sustain a small fraction of the
+// integer LDS atomic and plain-store rates, so grad_value is never
+// accumulated with them in the common path.
 
 struct __align__(16) BDesc {
   uint32_t off[4];  // element offsets of the corners (kOobElem outside the map)
-  float w[4];       // attn * bilinear weight
   float a, b;       // fractional parts of the index coordinate
   float aw, ah;     // attn * W_l, attn * H_l (chain rule through loc * W - 0.5)
 };
 
 template <typename T, int VEC, int NCG, int LPP>
-__global__ __launch_bounds__(kBlock) void bwd_kernel(const Params p) {
+__global__ __launch_bounds__(kBlock) void bwd_sample_kernel(const Params p) {
   __shared__ BDesc desc[kDescCap];
   __shared__ float3 res[kDescCap];
   __shared__ int32_t sH[kMaxLevels], sW[kMaxLevels], sS[kMaxLevels];
@@ -310,7 +325,6 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(const Params p) {
   const bool active = g < npairs;
 
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.value, p.value_elems * (uint32_t)T::size);
-  const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.grad_value, p.value_elems * 4u);
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.grad_out, (uint32_t)(p.pairs * p.D) * (uint32_t)T::size);
   const int nvec = p.D / VEC;
   uint32_t lane_elem[NCG];
@@ -332,13 +346,8 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(const Params p) {
       const Sample s = sample_geometry(p, P0 + gg, pc0 + pp, sH, sW, sS);
       const int l = (pc0 + pp) / p.K;
       BDesc d;
-      const float wa[2] = {1.0f - s.a, s.a};
-      const float wb[2] = {1.0f - s.b, s.b};
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        d.off[c] = s.off[c];
-        d.w[c] = s.A * wb[c >> 1] * wa[c & 1];
-      }
+      for (int c = 0; c < 4; ++c) d.off[c] = s.off[c];
       d.a = s.a;
       d.b = s.b;
       d.aw = s.A * (float)sW[l];
@@ -347,7 +356,6 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(const Params p) {
     }
     __syncthreads();
     if (active) {
-#pragma unroll 2
       for (int pp = 0; pp < pcn; ++pp) {
         const BDesc d = desc[pp * ppb + g];
         float dot[4];
@@ -370,16 +378,6 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(const Params p) {
         gx = group_sum<LPP>(gx, lpp);
         gy = group_sum<LPP>(gy, lpp);
         if (j == 0) res[pp * ppb + g] = make_float3(ga, d.aw * gx, d.ah * gy);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-#pragma unroll
-          for (int cg = 0; cg < NCG; ++cg) {
-            const uint32_t ob = (d.off[c] + lane_elem[cg]) * 4u;
-#pragma unroll
-            for (int e = 0; e < VEC; ++e)
-              __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(d.w[c] * G[cg][e], rg, ob + 4u * e, 0, 0);
-          }
-        }
       }
     }
     __syncthreads();
@@ -392,6 +390,320 @@ __global__ __launch_bounds__(kBlock) void bwd_kernel(const Params p) {
       *reinterpret_cast<float2 *>(p.grad_loc + 2 * gi) = make_float2(r.y, r.z);
     }
   }
+}
+
+// ------------------------------------------------------ tile binning (sort)
+
+// Corner rows/columns of a sample that lie inside the map, as the index
+// coordinate rule of sample_geometry defines them. Returns false when the
+// sample contributes nothing.
+struct Footprint {
+  int y0, x0;        // floor corner
+  bool r0, r1, c0, c1;  // rows y0, y0+1 and columns x0, x0+1 inside the map
+};
+
+__device__ __forceinline__ bool sample_footprint(float lx, float ly, int H, int W, Footprint &f) {
+  const float x = fmaf(lx, (float)W, -0.5f);
+  const float y = fmaf(ly, (float)H, -0.5f);
+  const bool inside = (x >= -1.0f) && (x < (float)W) && (y >= -1.0f) && (y < (float)H);
+  if (!inside) return false;
+  f.x0 = (int)floorf(x);
+  f.y0 = (int)floorf(y);
+  f.c0 = f.x0 >= 0;
+  f.c1 = f.x0 + 1 < W;
+  f.r0 = f.y0 >= 0;
+  f.r1 = f.y0 + 1 < H;
+  return true;
+}
+
+__device__ __forceinline__ void load_tile_levels(const Params &p, int32_t *sH, int32_t *sW, int32_t *sS,
+                                                 int32_t *sTW, int32_t *sToff) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int l = 0; l < kMaxLevels; ++l) {
+    if (tid == l) {
+      sH[l] = p.lv.H[l];
+      sW[l] = p.lv.W[l];
+      sS[l] = p.lv.start[l];
+      sTW[l] = p.lv.TW[l];
+      sToff[l] = p.lv.toff[l];
+    }
+  }
+}
+
+constexpr int kBinCap = 4096;  // LDS tile counters of one (image, head)
+
+// MODE 0 counts entries per tile; MODE 1 writes them in tile-major order.
+// Workgroup b covers image n, head m and queries [q0, q0 + qpb); its samples
+// are the (q, l, k) of that range, at most 4 per thread.
+template <int MODE>
+__global__ __launch_bounds__(kBlock) void bin_kernel(const Params p) {
+  __shared__ uint32_t cnt[kBinCap];
+  __shared__ int32_t sH[kMaxLevels], sW[kMaxLevels], sS[kMaxLevels], sTW[kMaxLevels], sToff[kMaxLevels];
+  load_tile_levels(p, sH, sW, sS, sTW, sToff);
+  const int tid = threadIdx.x;
+  const int qblocks = (p.Lq + p.qpb - 1) / p.qpb;
+  const int nm = blockIdx.x / qblocks;
+  const int qb = blockIdx.x - nm * qblocks;
+  const int n = nm / p.M, m = nm - n * p.M;
+  const int q0 = qb * p.qpb;
+  const int nsamp = (min(p.Lq, q0 + p.qpb) - q0) * p.LK;
+  const uint32_t tbase = (uint32_t)nm * (uint32_t)p.TPI;
+  const bool local = p.TPI <= kBinCap;
+  if (local)
+    for (int i = tid; i < p.TPI; i += kBlock) cnt[i] = 0;
+  __syncthreads();
+
+  // Up to four tiles per sample, in fixed slots (dy, dx) so that every array
+  // index below is a compile-time constant.
+  uint32_t sid[4], tl[4][4], rk[4][4];
+  bool has[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) has[r][k] = false;
+    const int i = tid + r * kBlock;
+    if (i >= nsamp) continue;
+    const int q = q0 + i / p.LK;
+    const int pt = i - (i / p.LK) * p.LK;
+    sid[r] = (uint32_t)((((int64_t)n * p.Lq + q) * p.M + m) * p.LK + pt);
+    const float2 xy = *reinterpret_cast<const float2 *>(p.loc + 2 * (int64_t)sid[r]);
+    const int l = pt / p.K;
+    Footprint f;
+    if (!sample_footprint(xy.x, xy.y, sH[l], sW[l], f)) continue;
+    // tile rows/columns touched by the in-map corners
+    const int ya = f.r0 ? f.y0 : f.y0 + 1, yb = f.r1 ? f.y0 + 1 : f.y0;
+    const int xa = f.c0 ? f.x0 : f.x0 + 1, xb = f.c1 ? f.x0 + 1 : f.x0;
+    const int tya = ya >> 3, tyb = yb >> 3, txa = xa >> 3, txb = xb >> 3;
+    const uint32_t lt = (uint32_t)sToff[l];
+#pragma unroll
+    for (int dy = 0; dy < 2; ++dy) {
+#pragma unroll
+      for (int dx = 0; dx < 2; ++dx) {
+        if ((dy && tyb == tya) || (dx && txb == txa)) continue;
+        const int k = dy * 2 + dx;
+        const uint32_t t = lt + (uint32_t)((dy ? tyb : tya) * sTW[l] + (dx ? txb : txa));
+        tl[r][k] = t;
+        has[r][k] = true;
+        if (local) {
+          rk[r][k] = atomicAdd(&cnt[t], 1u);
+        } else if (MODE == 0) {
+          atomicAdd(p.ws.tile_count + tbase + t, 1u);
+        } else {
+          const uint32_t pos = atomicAdd(p.ws.tile_cursor + tbase + t, 1u);
+          p.ws.entries[pos] = sid[r];
+        }
+      }
+    }
+  }
+  if (!local) return;
+  __syncthreads();
+  for (int i = tid; i < p.TPI; i += kBlock) {
+    const uint32_t c = cnt[i];
+    if (c == 0) continue;
+    if (MODE == 0) atomicAdd(p.ws.tile_count + tbase + i, c);
+    else cnt[i] = atomicAdd(p.ws.tile_cursor + tbase + i, c);
+  }
+  if (MODE == 0) return;
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (has[r][k]) p.ws.entries[cnt[tl[r][k]] + rk[r][k]] = sid[r];
+}
+
+// Exclusive scan of the tile counts (one workgroup of 1024 threads) and the
+// list of grad_value work items: each tile gives max(1, ceil(count /
+// kPartEntries)) items, so every tile, empty or not, is written.
+__global__ __launch_bounds__(1024) void scan_kernel(const Params p) {
+  __shared__ uint32_t wsum_c[16], wsum_p[16];
+  __shared__ uint32_t carry[2];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) carry[0] = carry[1] = 0;
+  __syncthreads();
+  for (int base = 0; base < p.T; base += 1024) {
+    const int t = base + tid;
+    const uint32_t c = t < p.T ? p.ws.tile_count[t] : 0u;
+    const uint32_t parts = t < p.T ? max(1u, (c + kPartEntries - 1) / kPartEntries) : 0u;
+    uint32_t ic = c, ip = parts;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t yc = __shfl_up(ic, o), yp = __shfl_up(ip, o);
+      if (lane >= o) { ic += yc; ip += yp; }
+    }
+    if (lane == 63) { wsum_c[wave] = ic; wsum_p[wave] = ip; }
+    __syncthreads();
+    uint32_t oc = carry[0], op = carry[1];
+    for (int w = 0; w < wave; ++w) { oc += wsum_c[w]; op += wsum_p[w]; }
+    if (t < p.T) {
+      const uint32_t start = oc + ic - c, wb = op + ip - parts;
+      p.ws.tile_start[t] = start;
+      p.ws.tile_cursor[t] = start;
+      for (uint32_t k = 0; k < parts; ++k) {
+        p.ws.work_tile[wb + k] = (uint32_t)t;
+        p.ws.work_part[wb + k] = k;
+      }
+    }
+    __syncthreads();
+    if (tid == 1023) { carry[0] = oc + ic; carry[1] = op + ip; }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    p.ws.tile_start[p.T] = carry[0];
+    *p.ws.n_work = carry[1];
+  }
+}
+
+__device__ __forceinline__ void decode_tile(const Params &p, uint32_t t, const int32_t *sToff, const int32_t *sTW,
+                                            int &n, int &m, int &l, int &ty, int &tx) {
+  const int nm = (int)(t / (uint32_t)p.TPI);
+  const int r = (int)(t - (uint32_t)nm * (uint32_t)p.TPI);
+  n = nm / p.M;
+  m = nm - n * p.M;
+  l = 0;
+  for (int k = 1; k < p.L; ++k)
+    if (sToff[k] <= r) l = k;
+  const int tl = r - sToff[l];
+  ty = tl / sTW[l];
+  tx = tl - ty * sTW[l];
+}
+
+// Zeroes the pixels of tiles whose entries are split over several work items
+// (their partial sums are then added with atomics).
+__global__ __launch_bounds__(kBlock) void zero_split_tiles_kernel(const Params p) {
+  __shared__ int32_t sH[kMaxLevels], sW[kMaxLevels], sS[kMaxLevels], sTW[kMaxLevels], sToff[kMaxLevels];
+  const uint32_t wi = blockIdx.x;
+  if (wi >= *p.ws.n_work || p.ws.work_part[wi] != 0) return;
+  const uint32_t t = p.ws.work_tile[wi];
+  if (p.ws.tile_start[t + 1] - p.ws.tile_start[t] <= (uint32_t)kPartEntries) return;
+  load_tile_levels(p, sH, sW, sS, sTW, sToff);
+  __syncthreads();
+  int n, m, l, ty, tx;
+  decode_tile(p, t, sToff, sTW, n, m, l, ty, tx);
+  for (int i = threadIdx.x; i < kTilePix * p.D; i += kBlock) {
+    const int pix = i / p.D, c = i - pix * p.D;
+    const int py = ty * kTile + (pix >> 3), px = tx * kTile + (pix & 7);
+    if (py < sH[l] && px < sW[l])
+      p.grad_value[(((int64_t)n * p.S + sS[l] + py * sW[l] + px) * p.M + m) * p.D + c] = 0.0f;
+  }
+}
+
+// grad_value of one tile (work item blockIdx.x) and one group of up to 64
+// channels (blockIdx.y). Thread (pixel, slice) owns CS channels of one pixel.
+template <typename T, int CS>
+__global__ __launch_bounds__(kBlock) void gv_kernel(const Params p) {
+  constexpr int kStage = 8192;                 // floats of staged grad_out rows
+  __shared__ float gst[kStage];
+  __shared__ uint32_t ent_pair[kBlock];
+  __shared__ uint16_t lst_e[4 * kBlock];
+  __shared__ float lst_w[4 * kBlock];
+  __shared__ uint32_t cnt[kTilePix], off[kTilePix + 1];
+  __shared__ int32_t sH[kMaxLevels], sW[kMaxLevels], sS[kMaxLevels], sTW[kMaxLevels], sToff[kMaxLevels];
+  const uint32_t wi = blockIdx.x;
+  if (wi >= *p.ws.n_work) return;
+  load_tile_levels(p, sH, sW, sS, sTW, sToff);
+  const int tid = threadIdx.x;
+  const uint32_t t = p.ws.work_tile[wi], part = p.ws.work_part[wi];
+  const uint32_t ea = p.ws.tile_start[t], eb = p.ws.tile_start[t + 1];
+  const bool split = eb - ea > (uint32_t)kPartEntries;
+  const uint32_t e0 = ea + part * kPartEntries, e1 = min(e0 + (uint32_t)kPartEntries, eb);
+  const int c0 = blockIdx.y * kChanGroup;
+  const int Dc = min(kChanGroup, p.D - c0);
+  const int Cs = (Dc + 3) >> 2;   // channels per thread (<= CS)
+  const int DcP = Cs * 4;         // staged row stride
+  const int E = min(kBlock, kStage / DcP);
+  const int pix = tid >> 2, slice = tid & 3;
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.grad_out, (uint32_t)(p.pairs * p.D) * (uint32_t)T::size);
+  __syncthreads();
+  int n, m, l, ty, tx;
+  decode_tile(p, t, sToff, sTW, n, m, l, ty, tx);
+  const int H = sH[l], W = sW[l];
+
+  float acc[CS];
+#pragma unroll
+  for (int c = 0; c < CS; ++c) acc[c] = 0.0f;
+
+  for (uint32_t cb = e0; cb < e1; cb += (uint32_t)E) {
+    const int ne = (int)min((uint32_t)E, e1 - cb);
+    if (tid < kTilePix) cnt[tid] = 0;
+    __syncthreads();
+    // corners of entry `tid` that fall in this tile, bucketed by pixel
+    bool cin[4] = {false, false, false, false};
+    uint32_t cpix[4], crk[4];
+    float cw[4];
+    if (tid < ne) {
+      const uint32_t s = p.ws.entries[cb + tid];
+      const uint32_t P = s / (uint32_t)p.LK;
+      ent_pair[tid] = P;
+      const float2 xy = *reinterpret_cast<const float2 *>(p.loc + 2 * (int64_t)s);
+      const float A = p.attn[s];
+      const float x = fmaf(xy.x, (float)W, -0.5f), y = fmaf(xy.y, (float)H, -0.5f);
+      const float xf = floorf(x), yf = floorf(y);
+      const float a = x - xf, b = y - yf;
+      const int x0 = (int)xf, y0 = (int)yf;
+      const float wa[2] = {1.0f - a, a}, wb[2] = {1.0f - b, b};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int cy = y0 + (c >> 1), cx = x0 + (c & 1);
+        if (cy < 0 || cy >= H || cx < 0 || cx >= W || (cy >> 3) != ty || (cx >> 3) != tx) continue;
+        cin[c] = true;
+        cpix[c] = (uint32_t)((cy & 7) * kTile + (cx & 7));
+        cw[c] = A * wb[c >> 1] * wa[c & 1];
+        crk[c] = atomicAdd(&cnt[cpix[c]], 1u);
+      }
+    }
+    __syncthreads();
+    // stage the entries' grad_out rows (this channel group) as float
+    for (int i = tid; i < ne * Dc; i += kBlock) {
+      const int e = i / Dc, c = i - e * Dc;
+      float v[1];
+      load_vals<T, 1>(ro, (ent_pair[e] * (uint32_t)p.D + (uint32_t)(c0 + c)) * (uint32_t)T::size, v);
+      gst[e * DcP + c] = v[0];
+    }
+    if (tid < 64) {
+      uint32_t v = cnt[tid];
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t y = __shfl_up(v, o);
+        if (tid >= o) v += y;
+      }
+      off[tid + 1] = v;
+      if (tid == 0) off[0] = 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (!cin[k]) continue;
+      const uint32_t j = off[cpix[k]] + crk[k];
+      lst_e[j] = (uint16_t)tid;
+      lst_w[j] = cw[k];
+    }
+    __syncthreads();
+    const uint32_t jb = off[pix], je = off[pix + 1];
+    for (uint32_t j = jb; j < je; ++j) {
+      const float w = lst_w[j];
+      const float *g = gst + lst_e[j] * DcP + slice * Cs;
+#pragma unroll
+      for (int c = 0; c < CS; ++c)
+        if (c < Cs) acc[c] = fmaf(w, g[c], acc[c]);
+    }
+    __syncthreads();
+  }
+  const int py = ty * kTile + (pix >> 3), px = tx * kTile + (pix & 7);
+  if (py >= H || px >= W) return;
+  float *dst = p.grad_value + (((int64_t)n * p.S + sS[l] + py * W + px) * p.M + m) * p.D + c0 + slice * Cs;
+#pragma unroll
+  for (int c = 0; c < CS; ++c) {
+    if (c >= Cs || slice * Cs + c >= Dc) continue;
+    if (split) atomicAdd(dst + c, acc[c]);
+    else dst[c] = acc[c];
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void zero_u32_kernel(uint32_t *ptr, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (i < n) ptr[i] = 0u;
 }
 
 // ------------------------------------------------------------- zero fill
@@ -419,18 +731,18 @@ KernelFn pick(bool fwd, int ncg, int lpp) {
   // Compile-time lane counts for the common 16-byte shapes (fp32 D=32 and
   // bf16 D=32), a runtime lane count otherwise.
   if (ncg == 1 && lpp == 8 && VEC * T::size == 16)
-    return fwd ? fwd_kernel<T, VEC, 1, 8> : bwd_kernel<T, VEC, 1, 8>;
+    return fwd ? fwd_kernel<T, VEC, 1, 8> : bwd_sample_kernel<T, VEC, 1, 8>;
   if (ncg == 1 && lpp == 4 && VEC * T::size == 16)
-    return fwd ? fwd_kernel<T, VEC, 1, 4> : bwd_kernel<T, VEC, 1, 4>;
+    return fwd ? fwd_kernel<T, VEC, 1, 4> : bwd_sample_kernel<T, VEC, 1, 4>;
   switch (ncg) {
-    case 1: return fwd ? fwd_kernel<T, VEC, 1, 0> : bwd_kernel<T, VEC, 1, 0>;
-    case 2: return fwd ? fwd_kernel<T, VEC, 2, 0> : bwd_kernel<T, VEC, 2, 0>;
-    case 4: return fwd ? fwd_kernel<T, VEC, 4, 0> : bwd_kernel<T, VEC, 4, 0>;
+    case 1: return fwd ? fwd_kernel<T, VEC, 1, 0> : bwd_sample_kernel<T, VEC, 1, 0>;
+    case 2: return fwd ? fwd_kernel<T, VEC, 2, 0> : bwd_sample_kernel<T, VEC, 2, 0>;
+    case 4: return fwd ? fwd_kernel<T, VEC, 4, 0> : bwd_sample_kernel<T, VEC, 4, 0>;
     default: break;
   }
   if constexpr (VEC == 1) {
-    if (ncg == 8) return fwd ? fwd_kernel<T, 1, 8, 0> : bwd_kernel<T, 1, 8, 0>;
-    if (ncg == 16) return fwd ? fwd_kernel<T, 1, 16, 0> : bwd_kernel<T, 1, 16, 0>;
+    if (ncg == 8) return fwd ? fwd_kernel<T, 1, 8, 0> : bwd_sample_kernel<T, 1, 8, 0>;
+    if (ncg == 16) return fwd ? fwd_kernel<T, 1, 16, 0> : bwd_sample_kernel<T, 1, 16, 0>;
   }
   return nullptr;
 }
@@ -453,7 +765,25 @@ KernelFn select(bool fwd, DType dt, const LaunchShape &s) {
   return nullptr;
 }
 
-hipError_t launch(bool fwd, const Params &p_in, DType dt, const LaunchShape &s, hipStream_t stream) {
+template <typename T>
+KernelFn pick_gv(int cs) {
+  switch (cs) {
+    case 1: return gv_kernel<T, 1>;
+    case 2: return gv_kernel<T, 2>;
+    case 4: return gv_kernel<T, 4>;
+    case 8: return gv_kernel<T, 8>;
+    default: return gv_kernel<T, 16>;
+  }
+}
+
+hipError_t launch_fn(const void *fn, int64_t blocks, int threads, int gy, Params &p, hipStream_t stream) {
+  if (blocks <= 0) return hipSuccess;
+  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+  void *args[] = {&p};
+  return hipLaunchKernel(fn, dim3((unsigned)blocks, (unsigned)gy), dim3(threads), args, 0, stream);
+}
+
+hipError_t launch_pairs(bool fwd, const Params &p_in, DType dt, const LaunchShape &s, hipStream_t stream) {
   KernelFn fn = select(fwd, dt, s);
   if (!fn) return hipErrorInvalidValue;
   Params p = p_in;
@@ -461,18 +791,13 @@ hipError_t launch(bool fwd, const Params &p_in, DType dt, const LaunchShape &s, 
   const int ppb = kBlock / s.lpp;
   p.pc = min(p.LK, max(1, kDescCap / ppb));
   const int64_t blocks = (p.pairs + ppb - 1) / ppb;
-  if (blocks <= 0) return hipSuccess;
-  if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-  void *args[] = {&p};
-  return hipLaunchKernel(reinterpret_cast<const void *>(fn), dim3((unsigned)blocks), dim3(kBlock), args, 0,
-                         stream);
+  return launch_fn(reinterpret_cast<const void *>(fn), blocks, kBlock, 1, p, stream);
 }
 
 }  // namespace
 
 LaunchShape choose_shape(int D, DType dt, uintptr_t align_bits) {
   const int esz = dt == DType::F32 ? 4 : 2;
-  LaunchShape s{1, 1, 1};
   // Widest access (16, 8, 4, 2 bytes) that divides a head's channels and the
   // pointers' alignment, while one pair fits in 64 lanes x 4 groups.
   for (int bytes = 16; bytes >= esz; bytes /= 2) {
@@ -484,8 +809,7 @@ LaunchShape choose_shape(int D, DType dt, uintptr_t align_bits) {
     while (lpp < nvec && lpp < 64) lpp *= 2;
     int ncg = 1;
     while (ncg * lpp < nvec) ncg *= 2;
-    s = LaunchShape{vec, lpp, ncg};
-    return s;
+    return LaunchShape{vec, lpp, ncg};
   }
   // Single-element lanes with up to 16 channel groups (D <= 1024).
   int ncg = 1;
@@ -495,12 +819,77 @@ LaunchShape choose_shape(int D, DType dt, uintptr_t align_bits) {
   return LaunchShape{1, lpp, ncg};
 }
 
-hipError_t launch_forward(const Params &p, DType dt, const LaunchShape &s, hipStream_t stream) {
-  return launch(true, p, dt, s, stream);
+void fill_tiles(LevelTable &lv, const int64_t *spatial_shapes, int64_t L, int32_t *TPI) {
+  int32_t acc = 0;
+  for (int64_t l = 0; l < L; ++l) {
+    lv.TH[l] = (int32_t)((spatial_shapes[2 * l] + kTile - 1) / kTile);
+    lv.TW[l] = (int32_t)((spatial_shapes[2 * l + 1] + kTile - 1) / kTile);
+    lv.toff[l] = acc;
+    acc += lv.TH[l] * lv.TW[l];
+  }
+  *TPI = acc;
 }
 
-hipError_t launch_backward(const Params &p, DType dt, const LaunchShape &s, hipStream_t stream) {
-  return launch(false, p, dt, s, stream);
+WorkspaceLayout workspace_layout(const int64_t *spatial_shapes, int64_t L, int64_t nimg, int64_t M, int64_t Lq,
+                                 int64_t K) {
+  int64_t tpi = 0;
+  for (int64_t l = 0; l < L; ++l)
+    tpi += ((spatial_shapes[2 * l] + kTile - 1) / kTile) * ((spatial_shapes[2 * l + 1] + kTile - 1) / kTile);
+  WorkspaceLayout w{};
+  w.T = nimg * M * tpi;
+  w.Emax = 4 * nimg * Lq * M * L * K;
+  w.Wmax = w.T + (w.Emax + kPartEntries - 1) / kPartEntries;
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  size_t o = 0;
+  w.off_count = o;   o = up(o + 4 * (size_t)w.T);
+  w.off_cursor = o;  o = up(o + 4 * (size_t)w.T);
+  w.off_start = o;   o = up(o + 4 * (size_t)(w.T + 1));
+  w.off_wtile = o;   o = up(o + 4 * (size_t)w.Wmax);
+  w.off_wpart = o;   o = up(o + 4 * (size_t)w.Wmax);
+  w.off_nwork = o;   o = up(o + 4);
+  w.off_entries = o; o = up(o + 4 * (size_t)w.Emax);
+  w.bytes = o;
+  return w;
+}
+
+hipError_t launch_forward(const Params &p, DType dt, const LaunchShape &s, hipStream_t stream) {
+  return launch_pairs(true, p, dt, s, stream);
+}
+
+hipError_t launch_backward(const Params &p_in, DType dt, const LaunchShape &s, hipStream_t stream) {
+  Params p = p_in;
+  p.qpb = max(1, 1024 / p.LK);
+  hipError_t e;
+  // 1. tile counters
+  {
+    uint32_t *ptr = p.ws.tile_count;
+    int64_t n = p.T;
+    void *args[] = {&ptr, &n};
+    e = hipLaunchKernel(reinterpret_cast<const void *>(zero_u32_kernel), dim3((unsigned)((n + kBlock - 1) / kBlock)),
+                        dim3(kBlock), args, 0, stream);
+    if (e != hipSuccess) return e;
+  }
+  // 2. grad_attn, grad_loc
+  if ((e = launch_pairs(false, p, dt, s, stream)) != hipSuccess) return e;
+  // 3. counting sort of (sample, tile) entries
+  const int64_t bin_blocks = (int64_t)p.N * p.M * ((p.Lq + p.qpb - 1) / p.qpb);
+  if ((e = launch_fn(reinterpret_cast<const void *>(bin_kernel<0>), bin_blocks, kBlock, 1, p, stream)) != hipSuccess)
+    return e;
+  if ((e = launch_fn(reinterpret_cast<const void *>(scan_kernel), 1, 1024, 1, p, stream)) != hipSuccess) return e;
+  if ((e = launch_fn(reinterpret_cast<const void *>(bin_kernel<1>), bin_blocks, kBlock, 1, p, stream)) != hipSuccess)
+    return e;
+  // 4. grad_value per tile
+  const int64_t wmax = p.T + (4 * p.pairs * p.LK + kPartEntries - 1) / kPartEntries;
+  if ((e = launch_fn(reinterpret_cast<const void *>(zero_split_tiles_kernel), wmax, kBlock, 1, p, stream)) !=
+      hipSuccess)
+    return e;
+  const int Dc = min(kChanGroup, p.D);
+  const int cs_need = (Dc + 3) / 4;
+  int cs = 1;
+  while (cs < cs_need) cs *= 2;
+  KernelFn gv = dt == DType::F32 ? pick_gv<F32>(cs) : pick_gv<BF16>(cs);
+  const int groups = (p.D + kChanGroup - 1) / kChanGroup;
+  return launch_fn(reinterpret_cast<const void *>(gv), wmax, kBlock, groups, p, stream);
 }
 
 hipError_t launch_zero(float *ptr, int64_t n, hipStream_t stream) {

@@ -27,8 +27,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["msda_backward", "msda_forward", "msda_status_string",
-                                    "msda_validate"]
+    assert declared_functions() == ["msda_backward", "msda_backward_workspace_size", "msda_forward",
+                                    "msda_status_string", "msda_validate"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(5):
+    for code in range(6):
         s = msda.msda_status_string(code)
         assert s.startswith("MSDA_")
     assert "unknown" in msda.msda_status_string(99)
@@ -101,20 +101,38 @@ def test_entry_points_reject_bad_pointers_before_any_hip_call():
     # null device pointers
     assert lib.msda_forward(None, ss, ls, A, A, A, *dims, 0, None) == 1
     assert lib.msda_forward(A, ss, ls, A, A, None, *dims, 0, None) == 1
-    assert lib.msda_backward(A, ss, ls, A, A, A, None, A, A, *dims, 0, None) == 1
-    assert lib.msda_backward(A, ss, ls, A, A, None, A, A, A, *dims, 0, None) == 1
+    W, WB = 0x100000, 1 << 40  # a workspace pointer and a size large enough for any check
+    assert lib.msda_backward(A, ss, ls, A, A, A, None, A, A, *dims, 0, W, WB, None) == 1
+    assert lib.msda_backward(A, ss, ls, A, A, None, A, A, A, *dims, 0, W, WB, None) == 1
+    # missing or short workspace
+    assert lib.msda_backward(A, ss, ls, A, A, A, A, A, A, *dims, 0, None, WB, None) == 5
+    assert lib.msda_backward(A, ss, ls, A, A, A, A, A, A, *dims, 0, W, 1024, None) == 5
+    assert lib.msda_backward(A, ss, ls, A, A, A, A, A, A, *dims, 0, W + 64, WB, None) == 3
     # misaligned: loc must be 8-byte aligned, fp32 arrays 4-byte, bf16 2-byte
     assert lib.msda_forward(A, ss, ls, A + 4, A, A, *dims, 0, None) == 3
     assert lib.msda_forward(A + 2, ss, ls, A, A, A, *dims, 0, None) == 3
     assert lib.msda_forward(A + 1, ss, ls, A, A, A, *dims, 1, None) == 3
-    assert lib.msda_backward(A, ss, ls, A, A, A, A + 2, A, A, *dims, 0, None) == 3
-    assert lib.msda_backward(A, ss, ls, A, A, A, A, A + 4, A, *dims, 0, None) == 3
+    assert lib.msda_backward(A, ss, ls, A, A, A, A + 2, A, A, *dims, 0, W, WB, None) == 3
+    assert lib.msda_backward(A, ss, ls, A, A, A, A, A + 4, A, *dims, 0, W, WB, None) == 3
     # invalid shapes reach no pointer at all
     assert lib.msda_forward(A, ss, ls, A, A, A, 1, 22223, 8, 32, 4, 22223, 17, 0, None) == 2
-    assert lib.msda_backward(A, ss, ls, A, A, A, A, A, A, 1, 22223, 8, 32, 4, 22223, 4, 5, None) == 2
+    assert lib.msda_backward(A, ss, ls, A, A, A, A, A, A, 1, 22223, 8, 32, 4, 22223, 4, 5, W, WB, None) == 2
     # an empty problem is a successful no-op without touching memory
     assert lib.msda_forward(None, ss, ls, None, None, None, 0, 22223, 8, 32, 4, 10, 4, 0, None) == 0
     assert lib.msda_forward(None, ss, ls, None, None, None, 1, 22223, 8, 32, 4, 0, 4, 0, None) == 0
+
+
+def test_workspace_size_and_overlapping_levels():
+    lib = binding.load_library()
+    n = msda.msda_backward_workspace_size(COCO, STARTS, 2, 22223, 8, 32, 4, 22223, 4)
+    samples = 2 * 22223 * 8 * 4 * 4
+    assert 16 * samples <= n <= 16 * samples + (1 << 20)
+    # overlapping level row ranges are rejected
+    ss = np.array([[4, 4], [2, 2]], dtype=np.int64)
+    ls = np.array([0, 14], dtype=np.int64)
+    assert lib.msda_validate(ss.ctypes.data, ls.ctypes.data, 1, 40, 1, 1, 2, 1, 1, 0) == 1
+    ls = np.array([0, 16], dtype=np.int64)
+    assert lib.msda_validate(ss.ctypes.data, ls.ctypes.data, 1, 40, 1, 1, 2, 1, 1, 0) == 0
 
 
 def test_binding_fails_loudly_without_the_library(monkeypatch):

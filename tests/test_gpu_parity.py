@@ -303,3 +303,39 @@ def test_autograd_wrapper_matches_entry_points():
     torch.cuda.synchronize()
     assert torch.allclose(value.grad, gv, atol=1e-6)
     assert torch.equal(loc.grad, gl) and torch.equal(attn.grad, ga)
+
+
+def test_crowded_tile_is_split():
+    """Thousands of samples on one 8x8 tile: its grad_value work is split over
+    several workgroups whose partial sums are combined."""
+    w = uniform_workload(N=1, shapes=((4, 5),), Lq=1500, M=2, D=32, K=4, seed=900, lo=0.0, hi=1.0,
+                         with_grad=True)
+    note("crowded tile: 6000 samples per head on a 4x5 map")
+    gv, gl, ga = (to_f64(t) for t in gpu_backward(w))
+    rgv, rgl, rga = msda_backward(*_oracle_args(w), w.grad_out)
+    assert_f32("grad_value", gv, rgv, atol=2e-5 * max(1.0, float(np.abs(rgv).max()) / 4))
+    assert_f32("grad_attn", ga, rga)
+    assert_grad_loc(gl, rgl, w.spatial_shapes)
+
+
+def test_levels_with_gaps():
+    """level_start may leave rows of value outside every level; their gradient is 0."""
+    rng = np.random.default_rng(950)
+    shapes = np.array([[5, 6], [3, 3]], dtype=np.int64)
+    starts = np.array([2, 40], dtype=np.int64)
+    S, M, D, Lq, K = 52, 2, 8, 11, 3
+    value = rng.standard_normal((1, S, M, D)).astype(np.float32)
+    loc = rng.uniform(-0.1, 1.1, (1, Lq, M, 2, K, 2)).astype(np.float32)
+    attn = rng.uniform(0, 1, (1, Lq, M, 2, K)).astype(np.float32)
+    G = rng.standard_normal((1, Lq, M, D)).astype(np.float32)
+    note("levels with gaps in value's rows")
+    args = [torch.from_numpy(a).cuda() for a in (value, loc, attn, G)]
+    out = msda.msda_forward(args[0], shapes, starts, args[1], args[2])
+    gv = torch.full_like(args[0], float("nan"))
+    gv, gl, ga = msda.msda_backward(args[0], shapes, starts, args[1], args[2], args[3], grad_value=gv)
+    torch.cuda.synchronize()
+    assert_f32("out", to_f64(out), msda_forward(value, shapes, starts, loc, attn))
+    rgv, rgl, rga = msda_backward(value, shapes, starts, loc, attn, G)
+    assert_f32("grad_value", to_f64(gv), rgv)
+    assert_f32("grad_attn", to_f64(ga), rga)
+    assert_grad_loc(to_f64(gl), rgl, shapes)
