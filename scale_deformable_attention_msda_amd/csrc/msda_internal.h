@@ -27,7 +27,7 @@ constexpr int kTilePix = kTile * kTile;
 // Entries (sample, tile) handled by one workgroup of the grad_value pass; a
 // tile with more entries is split into several work items whose partial sums
 // are combined with float atomics.
-constexpr int kPartEntries = 4096;
+constexpr int kPartEntries = 1024;
 // Channels handled by one grad_value work item.
 constexpr int kChanGroup = 64;
 
@@ -70,6 +70,7 @@ struct Params {
   int32_t TPI;           // tiles per (image, head) over all levels
   int32_t T;             // tiles of the launch: N * M * TPI
   int32_t qpb;           // queries per workgroup of the binning passes
+  int32_t gvec;          // grad_out rows allow 16-byte loads
   Workspace ws;
   LevelTable lv;
 };

@@ -431,14 +431,55 @@ __device__ __forceinline__ void load_tile_levels(const Params &p, int32_t *sH, i
   }
 }
 
-constexpr int kBinCap = 4096;  // LDS tile counters of one (image, head)
+constexpr int kBinCap = 2048;      // LDS tile counters of one (image, head)
+constexpr int kBinEntries = 4096;  // entries of one binning workgroup (1024 samples x 4)
+
+// In-place exclusive scan of n <= kBinCap counters in LDS by the whole
+// workgroup; returns the total.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t *a, int n, uint32_t *wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int per = (n + kBlock - 1) / kBlock;
+  const int b = tid * per;
+  uint32_t run = 0;
+  for (int i = 0; i < per; ++i)
+    if (b + i < n) run += a[b + i];
+  uint32_t v = run;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(v, o);
+    if (lane >= o) v += y;
+  }
+  if (lane == 63) wsum[wave] = v;
+  __syncthreads();
+  uint32_t base = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kBlock / 64; ++w) {
+    if (w < wave) base += wsum[w];
+    total += wsum[w];
+  }
+  uint32_t ex = base + v - run;
+  for (int i = 0; i < per; ++i)
+    if (b + i < n) {
+      const uint32_t c = a[b + i];
+      a[b + i] = ex;
+      ex += c;
+    }
+  __syncthreads();
+  return total;
+}
 
 // MODE 0 counts entries per tile; MODE 1 writes them in tile-major order.
 // Workgroup b covers image n, head m and queries [q0, q0 + qpb); its samples
-// are the (q, l, k) of that range, at most 4 per thread.
+// are the (q, l, k) of that range, at most 4 per thread. In MODE 1 the
+// workgroup first sorts its entries by tile in LDS, so that the global
+// writes of one tile's run are consecutive.
 template <int MODE>
 __global__ __launch_bounds__(kBlock) void bin_kernel(const Params p) {
   __shared__ uint32_t cnt[kBinCap];
+  __shared__ uint32_t gbase[MODE == 1 ? kBinCap : 1];
+  __shared__ uint32_t lsid[MODE == 1 ? kBinEntries : 1];
+  __shared__ uint32_t laddr[MODE == 1 ? kBinEntries : 1];
+  __shared__ uint32_t wsum[kBlock / 64];
   __shared__ int32_t sH[kMaxLevels], sW[kMaxLevels], sS[kMaxLevels], sTW[kMaxLevels], sToff[kMaxLevels];
   load_tile_levels(p, sH, sW, sS, sTW, sToff);
   const int tid = threadIdx.x;
@@ -498,19 +539,31 @@ __global__ __launch_bounds__(kBlock) void bin_kernel(const Params p) {
   }
   if (!local) return;
   __syncthreads();
-  for (int i = tid; i < p.TPI; i += kBlock) {
-    const uint32_t c = cnt[i];
-    if (c == 0) continue;
-    if (MODE == 0) atomicAdd(p.ws.tile_count + tbase + i, c);
-    else cnt[i] = atomicAdd(p.ws.tile_cursor + tbase + i, c);
+  if constexpr (MODE == 0) {
+    for (int i = tid; i < p.TPI; i += kBlock) {
+      const uint32_t c = cnt[i];
+      if (c) atomicAdd(p.ws.tile_count + tbase + i, c);
+    }
+  } else {
+    // reserve each tile's global run, then lay the entries out tile by tile
+    for (int i = tid; i < p.TPI; i += kBlock) {
+      const uint32_t c = cnt[i];
+      gbase[i] = c ? atomicAdd(p.ws.tile_cursor + tbase + i, c) : 0u;
+    }
+    __syncthreads();
+    const uint32_t nent = block_exclusive_scan(cnt, p.TPI, wsum);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (!has[r][k]) continue;
+        const uint32_t slot = cnt[tl[r][k]] + rk[r][k];
+        lsid[slot] = sid[r];
+        laddr[slot] = gbase[tl[r][k]] + rk[r][k];
+      }
+    __syncthreads();
+    for (uint32_t i = tid; i < nent; i += kBlock) p.ws.entries[laddr[i]] = lsid[i];
   }
-  if (MODE == 0) return;
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if (has[r][k]) p.ws.entries[cnt[tl[r][k]] + rk[r][k]] = sid[r];
 }
 
 // Exclusive scan of the tile counts (one workgroup of 1024 threads) and the
@@ -590,12 +643,16 @@ __global__ __launch_bounds__(kBlock) void zero_split_tiles_kernel(const Params p
 }
 
 // grad_value of one tile (work item blockIdx.x) and one group of up to 64
-// channels (blockIdx.y). Thread (pixel, slice) owns CS channels of one pixel.
+// channels (blockIdx.y). Per chunk of entries: the thread that owns an entry
+// loads its grad_out row slice (issued first, independent of the geometry),
+// computes the corners that fall in the tile and buckets them by pixel; then
+// thread (pixel, slice) sums the contributions to its CS channels of that
+// pixel in registers.
 template <typename T, int CS>
 __global__ __launch_bounds__(kBlock) void gv_kernel(const Params p) {
-  constexpr int kStage = 8192;                 // floats of staged grad_out rows
-  __shared__ float gst[kStage];
-  __shared__ uint32_t ent_pair[kBlock];
+  constexpr int kStage = 8192;  // floats of staged grad_out rows
+  constexpr int VG = 16 / T::size;  // elements of one 16-byte grad_out load
+  __shared__ __align__(16) float gst[kStage];
   __shared__ uint16_t lst_e[4 * kBlock];
   __shared__ float lst_w[4 * kBlock];
   __shared__ uint32_t cnt[kTilePix], off[kTilePix + 1];
@@ -611,9 +668,10 @@ __global__ __launch_bounds__(kBlock) void gv_kernel(const Params p) {
   const int c0 = blockIdx.y * kChanGroup;
   const int Dc = min(kChanGroup, p.D - c0);
   const int Cs = (Dc + 3) >> 2;   // channels per thread (<= CS)
-  const int DcP = Cs * 4;         // staged row stride
+  const int DcP = Cs * 4;         // staged row stride (floats)
   const int E = min(kBlock, kStage / DcP);
   const int pix = tid >> 2, slice = tid & 3;
+  const bool vec = p.gvec != 0 && Dc % VG == 0;
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.grad_out, (uint32_t)(p.pairs * p.D) * (uint32_t)T::size);
   __syncthreads();
   int n, m, l, ty, tx;
@@ -628,14 +686,32 @@ __global__ __launch_bounds__(kBlock) void gv_kernel(const Params p) {
     const int ne = (int)min((uint32_t)E, e1 - cb);
     if (tid < kTilePix) cnt[tid] = 0;
     __syncthreads();
-    // corners of entry `tid` that fall in this tile, bucketed by pixel
     bool cin[4] = {false, false, false, false};
     uint32_t cpix[4], crk[4];
     float cw[4];
     if (tid < ne) {
       const uint32_t s = p.ws.entries[cb + tid];
       const uint32_t P = s / (uint32_t)p.LK;
-      ent_pair[tid] = P;
+      float grow[4 * CS];
+#pragma unroll
+      for (int c = 0; c < 4 * CS; ++c) grow[c] = 0.0f;
+      const uint32_t gb = P * (uint32_t)p.D + (uint32_t)c0;
+      bool scalar = true;
+      if constexpr (4 * CS >= VG) {
+        if (vec) {
+          scalar = false;
+#pragma unroll
+          for (int k = 0; k < 4 * CS / VG; ++k)
+            if (k * VG < Dc)
+              load_vals<T, VG>(ro, (gb + (uint32_t)(k * VG)) * (uint32_t)T::size,
+                               *reinterpret_cast<float(*)[VG]>(&grow[k * VG]));
+        }
+      }
+      if (scalar) {
+#pragma unroll
+        for (int c = 0; c < 4 * CS; ++c)
+          if (c < Dc) load_vals<T, 1>(ro, (gb + (uint32_t)c) * (uint32_t)T::size, *reinterpret_cast<float(*)[1]>(&grow[c]));
+      }
       const float2 xy = *reinterpret_cast<const float2 *>(p.loc + 2 * (int64_t)s);
       const float A = p.attn[s];
       const float x = fmaf(xy.x, (float)W, -0.5f), y = fmaf(xy.y, (float)H, -0.5f);
@@ -652,15 +728,12 @@ __global__ __launch_bounds__(kBlock) void gv_kernel(const Params p) {
         cw[c] = A * wb[c >> 1] * wa[c & 1];
         crk[c] = atomicAdd(&cnt[cpix[c]], 1u);
       }
+      float4 *row = reinterpret_cast<float4 *>(gst + tid * DcP);
+#pragma unroll
+      for (int k = 0; k < CS; ++k)
+        if (k < Cs) row[k] = make_float4(grow[4 * k], grow[4 * k + 1], grow[4 * k + 2], grow[4 * k + 3]);
     }
     __syncthreads();
-    // stage the entries' grad_out rows (this channel group) as float
-    for (int i = tid; i < ne * Dc; i += kBlock) {
-      const int e = i / Dc, c = i - e * Dc;
-      float v[1];
-      load_vals<T, 1>(ro, (ent_pair[e] * (uint32_t)p.D + (uint32_t)(c0 + c)) * (uint32_t)T::size, v);
-      gst[e * DcP + c] = v[0];
-    }
     if (tid < 64) {
       uint32_t v = cnt[tid];
 #pragma unroll
@@ -681,24 +754,53 @@ __global__ __launch_bounds__(kBlock) void gv_kernel(const Params p) {
     }
     __syncthreads();
     const uint32_t jb = off[pix], je = off[pix + 1];
-    for (uint32_t j = jb; j < je; ++j) {
-      const float w = lst_w[j];
-      const float *g = gst + lst_e[j] * DcP + slice * Cs;
+    if ((Cs & 3) == 0) {
+      for (uint32_t j = jb; j < je; ++j) {
+        const float w = lst_w[j];
+        const float4 *g = reinterpret_cast<const float4 *>(gst + lst_e[j] * DcP + slice * Cs);
 #pragma unroll
-      for (int c = 0; c < CS; ++c)
-        if (c < Cs) acc[c] = fmaf(w, g[c], acc[c]);
+        for (int k = 0; k < CS / 4; ++k) {
+          if (4 * k >= Cs) continue;
+          const float4 v = g[k];
+          acc[4 * k] = fmaf(w, v.x, acc[4 * k]);
+          acc[4 * k + 1] = fmaf(w, v.y, acc[4 * k + 1]);
+          acc[4 * k + 2] = fmaf(w, v.z, acc[4 * k + 2]);
+          acc[4 * k + 3] = fmaf(w, v.w, acc[4 * k + 3]);
+        }
+      }
+    } else {
+      for (uint32_t j = jb; j < je; ++j) {
+        const float w = lst_w[j];
+        const float *g = gst + lst_e[j] * DcP + slice * Cs;
+#pragma unroll
+        for (int c = 0; c < CS; ++c)
+          if (c < Cs) acc[c] = fmaf(w, g[c], acc[c]);
+      }
     }
     __syncthreads();
   }
+  const int64_t row0 = (int64_t)n * p.S + sS[l];
+  if (split) {
+    // Partial sums of a split tile: add them channel-contiguously, so that one
+    // atomic instruction covers whole 64-byte segments of a pixel's row.
+#pragma unroll
+    for (int c = 0; c < CS; ++c)
+      if (c < Cs) gst[pix * DcP + slice * Cs + c] = acc[c];
+    __syncthreads();
+    for (int i = tid; i < kTilePix * Dc; i += kBlock) {
+      const int q = i / Dc, c = i - q * Dc;
+      const int py = ty * kTile + (q >> 3), px = tx * kTile + (q & 7);
+      if (py < H && px < W)
+        atomicAdd(p.grad_value + ((row0 + py * W + px) * p.M + m) * p.D + c0 + c, gst[q * DcP + c]);
+    }
+    return;
+  }
   const int py = ty * kTile + (pix >> 3), px = tx * kTile + (pix & 7);
   if (py >= H || px >= W) return;
-  float *dst = p.grad_value + (((int64_t)n * p.S + sS[l] + py * W + px) * p.M + m) * p.D + c0 + slice * Cs;
+  float *dst = p.grad_value + ((row0 + py * W + px) * p.M + m) * p.D + c0 + slice * Cs;
 #pragma unroll
-  for (int c = 0; c < CS; ++c) {
-    if (c >= Cs || slice * Cs + c >= Dc) continue;
-    if (split) atomicAdd(dst + c, acc[c]);
-    else dst[c] = acc[c];
-  }
+  for (int c = 0; c < CS; ++c)
+    if (c < Cs && slice * Cs + c < Dc) dst[c] = acc[c];
 }
 
 __global__ __launch_bounds__(kBlock) void zero_u32_kernel(uint32_t *ptr, int64_t n) {
@@ -859,6 +961,8 @@ hipError_t launch_forward(const Params &p, DType dt, const LaunchShape &s, hipSt
 hipError_t launch_backward(const Params &p_in, DType dt, const LaunchShape &s, hipStream_t stream) {
   Params p = p_in;
   p.qpb = max(1, 1024 / p.LK);
+  // 16-byte grad_out loads in the grad_value pass when rows and pointer allow
+  p.gvec = (s.vec * (dt == DType::F32 ? 4 : 2)) == 16 ? 1 : 0;
   hipError_t e;
   // 1. tile counters
   {
