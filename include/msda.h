@@ -108,7 +108,8 @@ msda_status msda_forward(const void *value, const int64_t *spatial_shapes,
  * Bytes of device workspace msda_backward needs for these sizes (the same
  * checks as msda_validate apply). The workspace holds a counting sort of the
  * samples by the 8x8-pixel tile of the value map they touch: a few counters
- * per tile plus four 32-bit entries per sample, about 16*N*Lq*M*L*K bytes.
+ * per tile plus up to four 16-byte entries per sample, about 64*N*Lq*M*L*K
+ * bytes.
  */
 msda_status msda_backward_workspace_size(const int64_t *spatial_shapes, const int64_t *level_start,
                                          int64_t N, int64_t S, int64_t M, int64_t D, int64_t L,

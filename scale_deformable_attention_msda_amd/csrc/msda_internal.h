@@ -42,13 +42,13 @@ struct LevelTable {
 
 // Backward scratch, carved out of the caller's workspace.
 struct Workspace {
-  uint32_t *tile_count;   // [T]   entries per tile
+  uint32_t *tile_count;   // [T+8] entries per tile, then eight work-shard counters
   uint32_t *tile_cursor;  // [T]   fill cursor of the scatter pass
   uint32_t *tile_start;   // [T+1] first entry of each tile
   uint32_t *work_tile;    // [Wmax] work items of the grad_value pass
   uint32_t *work_part;    // [Wmax]
   uint32_t *n_work;       // [1]
-  uint32_t *entries;      // [Emax] sample index of each (sample, tile) entry, tile-major
+  uint32_t *entries;      // [4*Emax] (sample, tile) entries, tile-major, 16-byte records
 };
 
 // One launch covers images [0, N) of the pointers below (the host offsets the

@@ -27,6 +27,7 @@
 //     sort of the samples (see the backward section).
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "msda_internal.h"
@@ -398,6 +399,7 @@ __global__ __launch_bounds__(kBlock) void bwd_sample_kernel(const Params p) {
 // coordinate rule of sample_geometry defines them. Returns false when the
 // sample contributes nothing.
 struct Footprint {
+  float x, y;        // index-space coordinate
   int y0, x0;        // floor corner
   bool r0, r1, c0, c1;  // rows y0, y0+1 and columns x0, x0+1 inside the map
 };
@@ -407,6 +409,8 @@ __device__ __forceinline__ bool sample_footprint(float lx, float ly, int H, int 
   const float y = fmaf(ly, (float)H, -0.5f);
   const bool inside = (x >= -1.0f) && (x < (float)W) && (y >= -1.0f) && (y < (float)H);
   if (!inside) return false;
+  f.x = x;
+  f.y = y;
   f.x0 = (int)floorf(x);
   f.y0 = (int)floorf(y);
   f.c0 = f.x0 >= 0;
@@ -432,54 +436,17 @@ __device__ __forceinline__ void load_tile_levels(const Params &p, int32_t *sH, i
 }
 
 constexpr int kBinCap = 2048;      // LDS tile counters of one (image, head)
-constexpr int kBinEntries = 4096;  // entries of one binning workgroup (1024 samples x 4)
 
-// In-place exclusive scan of n <= kBinCap counters in LDS by the whole
-// workgroup; returns the total.
-__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t *a, int n, uint32_t *wsum) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int per = (n + kBlock - 1) / kBlock;
-  const int b = tid * per;
-  uint32_t run = 0;
-  for (int i = 0; i < per; ++i)
-    if (b + i < n) run += a[b + i];
-  uint32_t v = run;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(v, o);
-    if (lane >= o) v += y;
-  }
-  if (lane == 63) wsum[wave] = v;
-  __syncthreads();
-  uint32_t base = 0, total = 0;
-#pragma unroll
-  for (int w = 0; w < kBlock / 64; ++w) {
-    if (w < wave) base += wsum[w];
-    total += wsum[w];
-  }
-  uint32_t ex = base + v - run;
-  for (int i = 0; i < per; ++i)
-    if (b + i < n) {
-      const uint32_t c = a[b + i];
-      a[b + i] = ex;
-      ex += c;
-    }
-  __syncthreads();
-  return total;
-}
-
-// MODE 0 counts entries per tile; MODE 1 writes them in tile-major order.
+// MODE 0 counts entries per tile; MODE 1 writes them in tile-major order as
+// 16-byte records {pair, x, y, attn} (x, y: the sample's index-space
+// coordinate), so the grad_value pass needs no access to loc or attn.
 // Workgroup b covers image n, head m and queries [q0, q0 + qpb); its samples
-// are the (q, l, k) of that range, at most 4 per thread. In MODE 1 the
-// workgroup first sorts its entries by tile in LDS, so that the global
-// writes of one tile's run are consecutive.
+// are the (q, l, k) of that range, at most 4 per thread. Tiles are numbered
+// head-major: ((m * N + n) * TPI) + tile within the (image, head).
 template <int MODE>
 __global__ __launch_bounds__(kBlock) void bin_kernel(const Params p) {
   __shared__ uint32_t cnt[kBinCap];
   __shared__ uint32_t gbase[MODE == 1 ? kBinCap : 1];
-  __shared__ uint32_t lsid[MODE == 1 ? kBinEntries : 1];
-  __shared__ uint32_t laddr[MODE == 1 ? kBinEntries : 1];
-  __shared__ uint32_t wsum[kBlock / 64];
   __shared__ int32_t sH[kMaxLevels], sW[kMaxLevels], sS[kMaxLevels], sTW[kMaxLevels], sToff[kMaxLevels];
   load_tile_levels(p, sH, sW, sS, sTW, sToff);
   const int tid = threadIdx.x;
@@ -489,15 +456,17 @@ __global__ __launch_bounds__(kBlock) void bin_kernel(const Params p) {
   const int n = nm / p.M, m = nm - n * p.M;
   const int q0 = qb * p.qpb;
   const int nsamp = (min(p.Lq, q0 + p.qpb) - q0) * p.LK;
-  const uint32_t tbase = (uint32_t)nm * (uint32_t)p.TPI;
+  const uint32_t tbase = ((uint32_t)m * (uint32_t)p.N + (uint32_t)n) * (uint32_t)p.TPI;
   const bool local = p.TPI <= kBinCap;
+  uint4 *rec_out = reinterpret_cast<uint4 *>(p.ws.entries);
   if (local)
     for (int i = tid; i < p.TPI; i += kBlock) cnt[i] = 0;
   __syncthreads();
 
   // Up to four tiles per sample, in fixed slots (dy, dx) so that every array
   // index below is a compile-time constant.
-  uint32_t sid[4], tl[4][4], rk[4][4];
+  uint4 rec[4];
+  uint32_t tl[4][4], rk[4][4];
   bool has[4][4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -505,13 +474,15 @@ __global__ __launch_bounds__(kBlock) void bin_kernel(const Params p) {
     for (int k = 0; k < 4; ++k) has[r][k] = false;
     const int i = tid + r * kBlock;
     if (i >= nsamp) continue;
-    const int q = q0 + i / p.LK;
-    const int pt = i - (i / p.LK) * p.LK;
-    sid[r] = (uint32_t)((((int64_t)n * p.Lq + q) * p.M + m) * p.LK + pt);
-    const float2 xy = *reinterpret_cast<const float2 *>(p.loc + 2 * (int64_t)sid[r]);
+    const int qi = i / p.LK;
+    const int pt = i - qi * p.LK;
+    const uint32_t P = (uint32_t)(((int64_t)n * p.Lq + q0 + qi) * p.M + m);
+    const int64_t sid = (int64_t)P * p.LK + pt;
+    const float2 xy = *reinterpret_cast<const float2 *>(p.loc + 2 * sid);
     const int l = pt / p.K;
     Footprint f;
     if (!sample_footprint(xy.x, xy.y, sH[l], sW[l], f)) continue;
+    if (MODE == 1) rec[r] = make_uint4(P, __float_as_uint(f.x), __float_as_uint(f.y), __float_as_uint(p.attn[sid]));
     // tile rows/columns touched by the in-map corners
     const int ya = f.r0 ? f.y0 : f.y0 + 1, yb = f.r1 ? f.y0 + 1 : f.y0;
     const int xa = f.c0 ? f.x0 : f.x0 + 1, xb = f.c1 ? f.x0 + 1 : f.x0;
@@ -531,8 +502,7 @@ __global__ __launch_bounds__(kBlock) void bin_kernel(const Params p) {
         } else if (MODE == 0) {
           atomicAdd(p.ws.tile_count + tbase + t, 1u);
         } else {
-          const uint32_t pos = atomicAdd(p.ws.tile_cursor + tbase + t, 1u);
-          p.ws.entries[pos] = sid[r];
+          rec_out[atomicAdd(p.ws.tile_cursor + tbase + t, 1u)] = rec[r];
         }
       }
     }
@@ -545,24 +515,17 @@ __global__ __launch_bounds__(kBlock) void bin_kernel(const Params p) {
       if (c) atomicAdd(p.ws.tile_count + tbase + i, c);
     }
   } else {
-    // reserve each tile's global run, then lay the entries out tile by tile
+    // reserve each tile's run once per workgroup, then write the records
     for (int i = tid; i < p.TPI; i += kBlock) {
       const uint32_t c = cnt[i];
-      gbase[i] = c ? atomicAdd(p.ws.tile_cursor + tbase + i, c) : 0u;
+      if (c) gbase[i] = atomicAdd(p.ws.tile_cursor + tbase + i, c);
     }
     __syncthreads();
-    const uint32_t nent = block_exclusive_scan(cnt, p.TPI, wsum);
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        if (!has[r][k]) continue;
-        const uint32_t slot = cnt[tl[r][k]] + rk[r][k];
-        lsid[slot] = sid[r];
-        laddr[slot] = gbase[tl[r][k]] + rk[r][k];
-      }
-    __syncthreads();
-    for (uint32_t i = tid; i < nent; i += kBlock) p.ws.entries[laddr[i]] = lsid[i];
+      for (int k = 0; k < 4; ++k)
+        if (has[r][k]) rec_out[gbase[tl[r][k]] + rk[r][k]] = rec[r];
   }
 }
 
@@ -610,10 +573,10 @@ __global__ __launch_bounds__(1024) void scan_kernel(const Params p) {
 
 __device__ __forceinline__ void decode_tile(const Params &p, uint32_t t, const int32_t *sToff, const int32_t *sTW,
                                             int &n, int &m, int &l, int &ty, int &tx) {
-  const int nm = (int)(t / (uint32_t)p.TPI);
-  const int r = (int)(t - (uint32_t)nm * (uint32_t)p.TPI);
-  n = nm / p.M;
-  m = nm - n * p.M;
+  const int mn = (int)(t / (uint32_t)p.TPI);
+  const int r = (int)(t - (uint32_t)mn * (uint32_t)p.TPI);
+  m = mn / p.N;
+  n = mn - m * p.N;
   l = 0;
   for (int k = 1; k < p.L; ++k)
     if (sToff[k] <= r) l = k;
@@ -623,184 +586,174 @@ __device__ __forceinline__ void decode_tile(const Params &p, uint32_t t, const i
 }
 
 // Zeroes the pixels of tiles whose entries are split over several work items
-// (their partial sums are then added with atomics).
+// (their partial sums are then added with atomics). Grid-stride over items.
 __global__ __launch_bounds__(kBlock) void zero_split_tiles_kernel(const Params p) {
   __shared__ int32_t sH[kMaxLevels], sW[kMaxLevels], sS[kMaxLevels], sTW[kMaxLevels], sToff[kMaxLevels];
-  const uint32_t wi = blockIdx.x;
-  if (wi >= *p.ws.n_work || p.ws.work_part[wi] != 0) return;
-  const uint32_t t = p.ws.work_tile[wi];
-  if (p.ws.tile_start[t + 1] - p.ws.tile_start[t] <= (uint32_t)kPartEntries) return;
   load_tile_levels(p, sH, sW, sS, sTW, sToff);
   __syncthreads();
-  int n, m, l, ty, tx;
-  decode_tile(p, t, sToff, sTW, n, m, l, ty, tx);
-  for (int i = threadIdx.x; i < kTilePix * p.D; i += kBlock) {
-    const int pix = i / p.D, c = i - pix * p.D;
-    const int py = ty * kTile + (pix >> 3), px = tx * kTile + (pix & 7);
-    if (py < sH[l] && px < sW[l])
-      p.grad_value[(((int64_t)n * p.S + sS[l] + py * sW[l] + px) * p.M + m) * p.D + c] = 0.0f;
+  const uint32_t nwork = *p.ws.n_work;
+  for (uint32_t wi = blockIdx.x; wi < nwork; wi += gridDim.x) {
+    if (p.ws.work_part[wi] != 0) continue;
+    const uint32_t t = p.ws.work_tile[wi];
+    if (p.ws.tile_start[t + 1] - p.ws.tile_start[t] <= (uint32_t)kPartEntries) continue;
+    int n, m, l, ty, tx;
+    decode_tile(p, t, sToff, sTW, n, m, l, ty, tx);
+    for (int i = threadIdx.x; i < kTilePix * p.D; i += kBlock) {
+      const int pix = i / p.D, c = i - pix * p.D;
+      const int py = ty * kTile + (pix >> 3), px = tx * kTile + (pix & 7);
+      if (py < sH[l] && px < sW[l])
+        p.grad_value[(((int64_t)n * p.S + sS[l] + py * sW[l] + px) * p.M + m) * p.D + c] = 0.0f;
+    }
   }
 }
 
-// grad_value of one tile (work item blockIdx.x) and one group of up to 64
-// channels (blockIdx.y). Per chunk of entries: the thread that owns an entry
-// loads its grad_out row slice (issued first, independent of the geometry),
-// computes the corners that fall in the tile and buckets them by pixel; then
-// thread (pixel, slice) sums the contributions to its CS channels of that
-// pixel in registers.
+// grad_value of one work item (blockIdx.x, last items first: the list ends
+// with the coarse levels' crowded tiles) and one group of up to 64 channels
+// (blockIdx.y). The item's entries (at most kPartEntries = 4 per thread) are
+// read once; each corner that falls in the tile is bucketed by pixel with LDS
+// integer atomics into a (pair, weight) list; then thread (pixel, slice) sums
+// its pixel's contributions to CS channels in registers, reading the grad_out
+// row slices straight from memory with several loads in flight.
 template <typename T, int CS>
 __global__ __launch_bounds__(kBlock) void gv_kernel(const Params p) {
-  constexpr int kStage = 8192;  // floats of staged grad_out rows
   constexpr int VG = 16 / T::size;  // elements of one 16-byte grad_out load
-  __shared__ __align__(16) float gst[kStage];
-  __shared__ uint16_t lst_e[4 * kBlock];
-  __shared__ float lst_w[4 * kBlock];
+  constexpr int kEPT = kPartEntries / kBlock;  // entries per thread
+  __shared__ __align__(16) uint2 lst[4 * kPartEntries];  // (pair, weight bits), pixel-major
   __shared__ uint32_t cnt[kTilePix], off[kTilePix + 1];
   __shared__ int32_t sH[kMaxLevels], sW[kMaxLevels], sS[kMaxLevels], sTW[kMaxLevels], sToff[kMaxLevels];
-  const uint32_t wi = blockIdx.x;
-  if (wi >= *p.ws.n_work) return;
+  const uint32_t nwork = *p.ws.n_work;
+  if (blockIdx.x >= nwork) return;
+  const uint32_t wi = nwork - 1 - blockIdx.x;
   load_tile_levels(p, sH, sW, sS, sTW, sToff);
   const int tid = threadIdx.x;
+  if (tid < kTilePix) cnt[tid] = 0;
   const uint32_t t = p.ws.work_tile[wi], part = p.ws.work_part[wi];
   const uint32_t ea = p.ws.tile_start[t], eb = p.ws.tile_start[t + 1];
   const bool split = eb - ea > (uint32_t)kPartEntries;
   const uint32_t e0 = ea + part * kPartEntries, e1 = min(e0 + (uint32_t)kPartEntries, eb);
-  const int c0 = blockIdx.y * kChanGroup;
-  const int Dc = min(kChanGroup, p.D - c0);
-  const int Cs = (Dc + 3) >> 2;   // channels per thread (<= CS)
-  const int DcP = Cs * 4;         // staged row stride (floats)
-  const int E = min(kBlock, kStage / DcP);
-  const int pix = tid >> 2, slice = tid & 3;
-  const bool vec = p.gvec != 0 && Dc % VG == 0;
-  const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.grad_out, (uint32_t)(p.pairs * p.D) * (uint32_t)T::size);
+  const uint4 *recs = reinterpret_cast<const uint4 *>(p.ws.entries);
+  uint4 rec[kEPT];
+#pragma unroll
+  for (int r = 0; r < kEPT; ++r) {
+    const uint32_t e = e0 + (uint32_t)(tid + r * kBlock);
+    rec[r] = e < e1 ? recs[e] : make_uint4(0xffffffffu, 0, 0, 0);
+  }
   __syncthreads();
   int n, m, l, ty, tx;
   decode_tile(p, t, sToff, sTW, n, m, l, ty, tx);
   const int H = sH[l], W = sW[l];
 
+  // corners of this thread's entries that fall in the tile, ranked per pixel
+  uint32_t cpix[kEPT][4], crk[kEPT][4];
+  float cw[kEPT][4];
+  bool cin[kEPT][4];
+#pragma unroll
+  for (int r = 0; r < kEPT; ++r) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c) cin[r][c] = false;
+    if (rec[r].x == 0xffffffffu) continue;
+    const float x = __uint_as_float(rec[r].y), y = __uint_as_float(rec[r].z), A = __uint_as_float(rec[r].w);
+    const float xf = floorf(x), yf = floorf(y);
+    const float a = x - xf, b = y - yf;
+    const int x0 = (int)xf, y0 = (int)yf;
+    const float wa[2] = {1.0f - a, a}, wb[2] = {1.0f - b, b};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int cy = y0 + (c >> 1), cx = x0 + (c & 1);
+      if (cy < 0 || cy >= H || cx < 0 || cx >= W || (cy >> 3) != ty || (cx >> 3) != tx) continue;
+      cin[r][c] = true;
+      cpix[r][c] = (uint32_t)((cy & 7) * kTile + (cx & 7));
+      cw[r][c] = A * wb[c >> 1] * wa[c & 1];
+      crk[r][c] = atomicAdd(&cnt[cpix[r][c]], 1u);
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {
+    uint32_t v = cnt[tid];
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(v, o);
+      if (tid >= o) v += y;
+    }
+    off[tid + 1] = v;
+    if (tid == 0) off[0] = 0;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kEPT; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (cin[r][c]) lst[off[cpix[r][c]] + crk[r][c]] = make_uint2(rec[r].x, __float_as_uint(cw[r][c]));
+  __syncthreads();
+
+  const int c0 = blockIdx.y * kChanGroup;
+  const int Dc = min(kChanGroup, p.D - c0);
+  const int Cs = (Dc + 3) >> 2;  // channels per thread (<= CS)
+  const int pix = tid >> 2, slice = tid & 3;
+  const int cbeg = c0 + slice * Cs;               // first channel of this thread
+  const int cnum = max(0, min(Cs, Dc - slice * Cs));  // channels it owns
+  const bool vec = p.gvec != 0 && Cs == CS && (Cs % VG) == 0;
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.grad_out, (uint32_t)(p.pairs * p.D) * (uint32_t)T::size);
   float acc[CS];
 #pragma unroll
   for (int c = 0; c < CS; ++c) acc[c] = 0.0f;
-
-  for (uint32_t cb = e0; cb < e1; cb += (uint32_t)E) {
-    const int ne = (int)min((uint32_t)E, e1 - cb);
-    if (tid < kTilePix) cnt[tid] = 0;
-    __syncthreads();
-    bool cin[4] = {false, false, false, false};
-    uint32_t cpix[4], crk[4];
-    float cw[4];
-    if (tid < ne) {
-      const uint32_t s = p.ws.entries[cb + tid];
-      const uint32_t P = s / (uint32_t)p.LK;
-      float grow[4 * CS];
+  const uint32_t jb = off[pix], je = off[pix + 1];
+  constexpr int U = 4;  // list entries in flight per thread
+  for (uint32_t j = jb; j < je; j += U) {
+    float g[U][CS];
+    float w[U];
 #pragma unroll
-      for (int c = 0; c < 4 * CS; ++c) grow[c] = 0.0f;
-      const uint32_t gb = P * (uint32_t)p.D + (uint32_t)c0;
-      bool scalar = true;
-      if constexpr (4 * CS >= VG) {
+    for (int u = 0; u < U; ++u) {
+      const bool ok = j + u < je;
+      const uint2 r2 = ok ? lst[j + u] : make_uint2(0, 0);
+      w[u] = __uint_as_float(r2.y);
+      // rows of absent slots read past the buffer (zeros); weight is 0 too
+      const uint32_t base = ok ? r2.x * (uint32_t)p.D + (uint32_t)cbeg : kOobElem;
+      if constexpr (CS >= VG) {
         if (vec) {
-          scalar = false;
 #pragma unroll
-          for (int k = 0; k < 4 * CS / VG; ++k)
-            if (k * VG < Dc)
-              load_vals<T, VG>(ro, (gb + (uint32_t)(k * VG)) * (uint32_t)T::size,
-                               *reinterpret_cast<float(*)[VG]>(&grow[k * VG]));
+          for (int q = 0; q < CS / VG; ++q)
+            load_vals<T, VG>(ro, (base + (uint32_t)(q * VG)) * (uint32_t)T::size,
+                             *reinterpret_cast<float(*)[VG]>(&g[u][q * VG]));
+          continue;
         }
       }
-      if (scalar) {
 #pragma unroll
-        for (int c = 0; c < 4 * CS; ++c)
-          if (c < Dc) load_vals<T, 1>(ro, (gb + (uint32_t)c) * (uint32_t)T::size, *reinterpret_cast<float(*)[1]>(&grow[c]));
-      }
-      const float2 xy = *reinterpret_cast<const float2 *>(p.loc + 2 * (int64_t)s);
-      const float A = p.attn[s];
-      const float x = fmaf(xy.x, (float)W, -0.5f), y = fmaf(xy.y, (float)H, -0.5f);
-      const float xf = floorf(x), yf = floorf(y);
-      const float a = x - xf, b = y - yf;
-      const int x0 = (int)xf, y0 = (int)yf;
-      const float wa[2] = {1.0f - a, a}, wb[2] = {1.0f - b, b};
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int cy = y0 + (c >> 1), cx = x0 + (c & 1);
-        if (cy < 0 || cy >= H || cx < 0 || cx >= W || (cy >> 3) != ty || (cx >> 3) != tx) continue;
-        cin[c] = true;
-        cpix[c] = (uint32_t)((cy & 7) * kTile + (cx & 7));
-        cw[c] = A * wb[c >> 1] * wa[c & 1];
-        crk[c] = atomicAdd(&cnt[cpix[c]], 1u);
-      }
-      float4 *row = reinterpret_cast<float4 *>(gst + tid * DcP);
-#pragma unroll
-      for (int k = 0; k < CS; ++k)
-        if (k < Cs) row[k] = make_float4(grow[4 * k], grow[4 * k + 1], grow[4 * k + 2], grow[4 * k + 3]);
+      for (int c = 0; c < CS; ++c)
+        load_vals<T, 1>(ro, (c < cnum ? base + (uint32_t)c : kOobElem) * (uint32_t)T::size,
+                        *reinterpret_cast<float(*)[1]>(&g[u][c]));
     }
-    __syncthreads();
-    if (tid < 64) {
-      uint32_t v = cnt[tid];
 #pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(v, o);
-        if (tid >= o) v += y;
-      }
-      off[tid + 1] = v;
-      if (tid == 0) off[0] = 0;
-    }
-    __syncthreads();
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (!cin[k]) continue;
-      const uint32_t j = off[cpix[k]] + crk[k];
-      lst_e[j] = (uint16_t)tid;
-      lst_w[j] = cw[k];
-    }
-    __syncthreads();
-    const uint32_t jb = off[pix], je = off[pix + 1];
-    if ((Cs & 3) == 0) {
-      for (uint32_t j = jb; j < je; ++j) {
-        const float w = lst_w[j];
-        const float4 *g = reinterpret_cast<const float4 *>(gst + lst_e[j] * DcP + slice * Cs);
-#pragma unroll
-        for (int k = 0; k < CS / 4; ++k) {
-          if (4 * k >= Cs) continue;
-          const float4 v = g[k];
-          acc[4 * k] = fmaf(w, v.x, acc[4 * k]);
-          acc[4 * k + 1] = fmaf(w, v.y, acc[4 * k + 1]);
-          acc[4 * k + 2] = fmaf(w, v.z, acc[4 * k + 2]);
-          acc[4 * k + 3] = fmaf(w, v.w, acc[4 * k + 3]);
-        }
-      }
-    } else {
-      for (uint32_t j = jb; j < je; ++j) {
-        const float w = lst_w[j];
-        const float *g = gst + lst_e[j] * DcP + slice * Cs;
-#pragma unroll
-        for (int c = 0; c < CS; ++c)
-          if (c < Cs) acc[c] = fmaf(w, g[c], acc[c]);
-      }
-    }
-    __syncthreads();
+      for (int c = 0; c < CS; ++c) acc[c] = fmaf(w[u], g[u][c], acc[c]);
   }
+
   const int64_t row0 = (int64_t)n * p.S + sS[l];
   if (split) {
     // Partial sums of a split tile: add them channel-contiguously, so that one
     // atomic instruction covers whole 64-byte segments of a pixel's row.
+    __syncthreads();
+    float *stage = reinterpret_cast<float *>(lst);
+    const int DcP = Cs * 4;
 #pragma unroll
     for (int c = 0; c < CS; ++c)
-      if (c < Cs) gst[pix * DcP + slice * Cs + c] = acc[c];
+      if (c < Cs) stage[pix * DcP + slice * Cs + c] = acc[c];
     __syncthreads();
     for (int i = tid; i < kTilePix * Dc; i += kBlock) {
       const int q = i / Dc, c = i - q * Dc;
       const int py = ty * kTile + (q >> 3), px = tx * kTile + (q & 7);
       if (py < H && px < W)
-        atomicAdd(p.grad_value + ((row0 + py * W + px) * p.M + m) * p.D + c0 + c, gst[q * DcP + c]);
+        atomicAdd(p.grad_value + ((row0 + py * W + px) * p.M + m) * p.D + c0 + c, stage[q * DcP + c]);
     }
     return;
   }
   const int py = ty * kTile + (pix >> 3), px = tx * kTile + (pix & 7);
   if (py >= H || px >= W) return;
-  float *dst = p.grad_value + ((row0 + py * W + px) * p.M + m) * p.D + c0 + slice * Cs;
+  float *dst = p.grad_value + ((row0 + py * W + px) * p.M + m) * p.D + cbeg;
 #pragma unroll
   for (int c = 0; c < CS; ++c)
-    if (c < Cs && slice * Cs + c < Dc) dst[c] = acc[c];
+    if (c < cnum) dst[c] = acc[c];
 }
 
 __global__ __launch_bounds__(kBlock) void zero_u32_kernel(uint32_t *ptr, int64_t n) {
@@ -943,13 +896,13 @@ WorkspaceLayout workspace_layout(const int64_t *spatial_shapes, int64_t L, int64
   w.Wmax = w.T + (w.Emax + kPartEntries - 1) / kPartEntries;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   size_t o = 0;
-  w.off_count = o;   o = up(o + 4 * (size_t)w.T);
+  w.off_count = o;   o = up(o + 4 * (size_t)(w.T + 8));
   w.off_cursor = o;  o = up(o + 4 * (size_t)w.T);
   w.off_start = o;   o = up(o + 4 * (size_t)(w.T + 1));
   w.off_wtile = o;   o = up(o + 4 * (size_t)w.Wmax);
   w.off_wpart = o;   o = up(o + 4 * (size_t)w.Wmax);
   w.off_nwork = o;   o = up(o + 4);
-  w.off_entries = o; o = up(o + 4 * (size_t)w.Emax);
+  w.off_entries = o; o = up(o + 16 * (size_t)w.Emax);
   w.bytes = o;
   return w;
 }
@@ -966,8 +919,8 @@ hipError_t launch_backward(const Params &p_in, DType dt, const LaunchShape &s, h
   hipError_t e;
   // 1. tile counters
   {
-    uint32_t *ptr = p.ws.tile_count;
-    int64_t n = p.T;
+    uint32_t *ptr = p.ws.tile_count;  // T counters and the eight work-shard counters
+    int64_t n = p.T + 8;
     void *args[] = {&ptr, &n};
     e = hipLaunchKernel(reinterpret_cast<const void *>(zero_u32_kernel), dim3((unsigned)((n + kBlock - 1) / kBlock)),
                         dim3(kBlock), args, 0, stream);
@@ -984,8 +937,8 @@ hipError_t launch_backward(const Params &p_in, DType dt, const LaunchShape &s, h
     return e;
   // 4. grad_value per tile
   const int64_t wmax = p.T + (4 * p.pairs * p.LK + kPartEntries - 1) / kPartEntries;
-  if ((e = launch_fn(reinterpret_cast<const void *>(zero_split_tiles_kernel), wmax, kBlock, 1, p, stream)) !=
-      hipSuccess)
+  if ((e = launch_fn(reinterpret_cast<const void *>(zero_split_tiles_kernel), std::min<int64_t>(wmax, 1024), kBlock, 1,
+                     p, stream)) != hipSuccess)
     return e;
   const int Dc = min(kChanGroup, p.D);
   const int cs_need = (Dc + 3) / 4;
