@@ -168,6 +168,7 @@ msda_status msda_backward(const void *value, const int64_t *spatial_shapes, cons
   p.ws.work_tile = reinterpret_cast<uint32_t *>(ws + wl.off_wtile);
   p.ws.work_part = reinterpret_cast<uint32_t *>(ws + wl.off_wpart);
   p.ws.n_work = reinterpret_cast<uint32_t *>(ws + wl.off_nwork);
+  p.ws.split_list = reinterpret_cast<uint32_t *>(ws + wl.off_split);
   p.ws.entries = reinterpret_cast<uint32_t *>(ws + wl.off_entries);
   for (int64_t n0 = 0; n0 < N; n0 += step) {
     const int64_t nb = std::min(step, N - n0);

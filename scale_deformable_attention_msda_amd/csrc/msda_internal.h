@@ -42,12 +42,13 @@ struct LevelTable {
 
 // Backward scratch, carved out of the caller's workspace.
 struct Workspace {
-  uint32_t *tile_count;   // [T+8] entries per tile, then eight work-shard counters
+  uint32_t *tile_count;   // [T+8] entries per tile; [T] counts split tiles
   uint32_t *tile_cursor;  // [T]   fill cursor of the scatter pass
   uint32_t *tile_start;   // [T+1] first entry of each tile
   uint32_t *work_tile;    // [Wmax] work items of the grad_value pass
   uint32_t *work_part;    // [Wmax]
   uint32_t *n_work;       // [1]
+  uint32_t *split_list;   // [T] tiles whose entries span several work items
   uint32_t *entries;      // [4*Emax] (sample, tile) entries, tile-major, 16-byte records
 };
 
@@ -71,6 +72,7 @@ struct Params {
   int32_t T;             // tiles of the launch: N * M * TPI
   int32_t qpb;           // queries per workgroup of the binning passes
   int32_t gvec;          // grad_out rows allow 16-byte loads
+  int32_t gv_blocks;     // grad_value blocks of the fused backward launch
   Workspace ws;
   LevelTable lv;
 };
@@ -89,7 +91,7 @@ LaunchShape choose_shape(int D, DType dt, uintptr_t align_bits);
 // Tile table and workspace layout of a launch covering `nimg` images.
 struct WorkspaceLayout {
   int64_t T, Wmax, Emax;
-  size_t off_count, off_cursor, off_start, off_wtile, off_wpart, off_nwork, off_entries, bytes;
+  size_t off_count, off_cursor, off_start, off_wtile, off_wpart, off_nwork, off_split, off_entries, bytes;
 };
 WorkspaceLayout workspace_layout(const int64_t *spatial_shapes, int64_t L, int64_t nimg, int64_t M,
                                  int64_t Lq, int64_t K);

@@ -309,17 +309,22 @@ struct __align__(16) BDesc {
   float aw, ah;     // attn * W_l, attn * H_l (chain rule through loc * W - 0.5)
 };
 
+constexpr size_t kSampleSmem = kDescCap * sizeof(BDesc) + kDescCap * sizeof(float3) + 3 * kMaxLevels * 4;
+
+// grad_attn and grad_loc of the pairs of logical block `block` (of `nblocks`),
+// with LDS carved from `smem` (kSampleSmem bytes).
 template <typename T, int VEC, int NCG, int LPP>
-__global__ __launch_bounds__(kBlock) void bwd_sample_kernel(const Params p) {
-  __shared__ BDesc desc[kDescCap];
-  __shared__ float3 res[kDescCap];
-  __shared__ int32_t sH[kMaxLevels], sW[kMaxLevels], sS[kMaxLevels];
+__device__ __forceinline__ void bwd_sample_body(const Params &p, int block, int nblocks, unsigned char *smem) {
+  BDesc *desc = reinterpret_cast<BDesc *>(smem);
+  float3 *res = reinterpret_cast<float3 *>(smem + kDescCap * sizeof(BDesc));
+  int32_t *sH = reinterpret_cast<int32_t *>(smem + kDescCap * (sizeof(BDesc) + sizeof(float3)));
+  int32_t *sW = sH + kMaxLevels, *sS = sW + kMaxLevels;
   load_levels(p, sH, sW, sS);
 
   const int tid = threadIdx.x;
   const int lpp = LPP > 0 ? LPP : p.lpp;
   const int ppb = kBlock / lpp;
-  const int64_t P0 = (int64_t)xcd_remap(blockIdx.x, gridDim.x) * ppb;
+  const int64_t P0 = (int64_t)xcd_remap(block, nblocks) * ppb;
   const int npairs = (int)min((int64_t)ppb, p.pairs - P0);
   const int g = tid / lpp;
   const int j = tid - g * lpp;
@@ -393,6 +398,12 @@ __global__ __launch_bounds__(kBlock) void bwd_sample_kernel(const Params p) {
   }
 }
 
+template <typename T, int VEC, int NCG, int LPP>
+__global__ __launch_bounds__(kBlock) void bwd_sample_kernel(const Params p) {
+  __shared__ __align__(16) unsigned char smem[kSampleSmem];
+  bwd_sample_body<T, VEC, NCG, LPP>(p, blockIdx.x, gridDim.x, smem);
+}
+
 // ------------------------------------------------------ tile binning (sort)
 
 // Corner rows/columns of a sample that lie inside the map, as the index
@@ -443,6 +454,10 @@ constexpr int kBinCap = 2048;      // LDS tile counters of one (image, head)
 // Workgroup b covers image n, head m and queries [q0, q0 + qpb); its samples
 // are the (q, l, k) of that range, at most 4 per thread. Tiles are numbered
 // head-major: ((m * N + n) * TPI) + tile within the (image, head).
+__device__ __forceinline__ void zero_split_body(const Params &p, int block, int nblocks, const int32_t *sH,
+                                                const int32_t *sW, const int32_t *sS, const int32_t *sTW,
+                                                const int32_t *sToff);
+
 template <int MODE>
 __global__ __launch_bounds__(kBlock) void bin_kernel(const Params p) {
   __shared__ uint32_t cnt[kBinCap];
@@ -451,6 +466,13 @@ __global__ __launch_bounds__(kBlock) void bin_kernel(const Params p) {
   load_tile_levels(p, sH, sW, sS, sTW, sToff);
   const int tid = threadIdx.x;
   const int qblocks = (p.Lq + p.qpb - 1) / p.qpb;
+  const int bin_blocks = p.N * p.M * qblocks;
+  if (MODE == 1 && (int)blockIdx.x >= bin_blocks) {
+    // the scatter launch carries extra workgroups that clear the split tiles
+    __syncthreads();
+    zero_split_body(p, (int)blockIdx.x - bin_blocks, (int)gridDim.x - bin_blocks, sH, sW, sS, sTW, sToff);
+    return;
+  }
   const int nm = blockIdx.x / qblocks;
   const int qb = blockIdx.x - nm * qblocks;
   const int n = nm / p.M, m = nm - n * p.M;
@@ -556,6 +578,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(const Params p) {
       const uint32_t start = oc + ic - c, wb = op + ip - parts;
       p.ws.tile_start[t] = start;
       p.ws.tile_cursor[t] = start;
+      if (parts > 1) p.ws.split_list[atomicAdd(p.ws.tile_count + p.T, 1u)] = (uint32_t)t;
       for (uint32_t k = 0; k < parts; ++k) {
         p.ws.work_tile[wb + k] = (uint32_t)t;
         p.ws.work_part[wb + k] = k;
@@ -586,20 +609,17 @@ __device__ __forceinline__ void decode_tile(const Params &p, uint32_t t, const i
 }
 
 // Zeroes the pixels of tiles whose entries are split over several work items
-// (their partial sums are then added with atomics). Grid-stride over items.
-__global__ __launch_bounds__(kBlock) void zero_split_tiles_kernel(const Params p) {
-  __shared__ int32_t sH[kMaxLevels], sW[kMaxLevels], sS[kMaxLevels], sTW[kMaxLevels], sToff[kMaxLevels];
-  load_tile_levels(p, sH, sW, sS, sTW, sToff);
-  __syncthreads();
-  const uint32_t nwork = *p.ws.n_work;
-  for (uint32_t wi = blockIdx.x; wi < nwork; wi += gridDim.x) {
-    if (p.ws.work_part[wi] != 0) continue;
-    const uint32_t t = p.ws.work_tile[wi];
-    if (p.ws.tile_start[t + 1] - p.ws.tile_start[t] <= (uint32_t)kPartEntries) continue;
+// (their partial sums are added with atomics): split tiles i = block,
+// block + nblocks, ... of the list the scan wrote.
+__device__ __forceinline__ void zero_split_body(const Params &p, int block, int nblocks, const int32_t *sH,
+                                                const int32_t *sW, const int32_t *sS, const int32_t *sTW,
+                                                const int32_t *sToff) {
+  const uint32_t nsplit = p.ws.tile_count[p.T];
+  for (uint32_t i = (uint32_t)block; i < nsplit; i += (uint32_t)nblocks) {
     int n, m, l, ty, tx;
-    decode_tile(p, t, sToff, sTW, n, m, l, ty, tx);
-    for (int i = threadIdx.x; i < kTilePix * p.D; i += kBlock) {
-      const int pix = i / p.D, c = i - pix * p.D;
+    decode_tile(p, p.ws.split_list[i], sToff, sTW, n, m, l, ty, tx);
+    for (int k = threadIdx.x; k < kTilePix * p.D; k += kBlock) {
+      const int pix = k / p.D, c = k - pix * p.D;
       const int py = ty * kTile + (pix >> 3), px = tx * kTile + (pix & 7);
       if (py < sH[l] && px < sW[l])
         p.grad_value[(((int64_t)n * p.S + sS[l] + py * sW[l] + px) * p.M + m) * p.D + c] = 0.0f;
@@ -614,16 +634,20 @@ __global__ __launch_bounds__(kBlock) void zero_split_tiles_kernel(const Params p
 // integer atomics into a (pair, weight) list; then thread (pixel, slice) sums
 // its pixel's contributions to CS channels in registers, reading the grad_out
 // row slices straight from memory with several loads in flight.
+constexpr size_t kGvSmem = 4 * kPartEntries * sizeof(uint2) + (2 * kTilePix + 1) * 4 + 5 * kMaxLevels * 4;
+
 template <typename T, int CS>
-__global__ __launch_bounds__(kBlock) void gv_kernel(const Params p) {
+__device__ __forceinline__ void gv_body(const Params &p, uint32_t bx, int cgroup, unsigned char *smem) {
   constexpr int VG = 16 / T::size;  // elements of one 16-byte grad_out load
   constexpr int kEPT = kPartEntries / kBlock;  // entries per thread
-  __shared__ __align__(16) uint2 lst[4 * kPartEntries];  // (pair, weight bits), pixel-major
-  __shared__ uint32_t cnt[kTilePix], off[kTilePix + 1];
-  __shared__ int32_t sH[kMaxLevels], sW[kMaxLevels], sS[kMaxLevels], sTW[kMaxLevels], sToff[kMaxLevels];
+  uint2 *lst = reinterpret_cast<uint2 *>(smem);  // (pair, weight bits), pixel-major
+  uint32_t *cnt = reinterpret_cast<uint32_t *>(smem + 4 * kPartEntries * sizeof(uint2));
+  uint32_t *off = cnt + kTilePix;
+  int32_t *sH = reinterpret_cast<int32_t *>(off + kTilePix + 1);
+  int32_t *sW = sH + kMaxLevels, *sS = sW + kMaxLevels, *sTW = sS + kMaxLevels, *sToff = sTW + kMaxLevels;
   const uint32_t nwork = *p.ws.n_work;
-  if (blockIdx.x >= nwork) return;
-  const uint32_t wi = nwork - 1 - blockIdx.x;
+  if (bx >= nwork) return;
+  const uint32_t wi = nwork - 1 - bx;
   load_tile_levels(p, sH, sW, sS, sTW, sToff);
   const int tid = threadIdx.x;
   if (tid < kTilePix) cnt[tid] = 0;
@@ -686,7 +710,7 @@ __global__ __launch_bounds__(kBlock) void gv_kernel(const Params p) {
       if (cin[r][c]) lst[off[cpix[r][c]] + crk[r][c]] = make_uint2(rec[r].x, __float_as_uint(cw[r][c]));
   __syncthreads();
 
-  const int c0 = blockIdx.y * kChanGroup;
+  const int c0 = cgroup * kChanGroup;
   const int Dc = min(kChanGroup, p.D - c0);
   const int Cs = (Dc + 3) >> 2;  // channels per thread (<= CS)
   const int pix = tid >> 2, slice = tid & 3;
@@ -754,6 +778,26 @@ __global__ __launch_bounds__(kBlock) void gv_kernel(const Params p) {
 #pragma unroll
   for (int c = 0; c < CS; ++c)
     if (c < cnum) dst[c] = acc[c];
+}
+
+template <typename T, int CS>
+__global__ __launch_bounds__(kBlock) void gv_kernel(const Params p) {
+  __shared__ __align__(16) unsigned char smem[kGvSmem];
+  gv_body<T, CS>(p, blockIdx.x, blockIdx.y, smem);
+}
+
+// The grad_value work items and the sample-gradient blocks in one launch: the
+// two are independent, so the sample gradients fill the machine while the
+// crowded tiles' items finish. Blocks [0, gv_blocks) are grad_value items
+// (one channel group when D <= 64), the rest run bwd_sample_body.
+template <typename T, int VEC, int NCG, int LPP, int CS>
+__global__ __launch_bounds__(kBlock) void bwd_fused_kernel(const Params p) {
+  constexpr size_t kSmem = kGvSmem > kSampleSmem ? kGvSmem : kSampleSmem;
+  __shared__ __align__(16) unsigned char smem[kSmem];
+  if ((int)blockIdx.x < p.gv_blocks)
+    gv_body<T, CS>(p, blockIdx.x, 0, smem);
+  else
+    bwd_sample_body<T, VEC, NCG, LPP>(p, (int)blockIdx.x - p.gv_blocks, (int)gridDim.x - p.gv_blocks, smem);
 }
 
 __global__ __launch_bounds__(kBlock) void zero_u32_kernel(uint32_t *ptr, int64_t n) {
@@ -902,6 +946,7 @@ WorkspaceLayout workspace_layout(const int64_t *spatial_shapes, int64_t L, int64
   w.off_wtile = o;   o = up(o + 4 * (size_t)w.Wmax);
   w.off_wpart = o;   o = up(o + 4 * (size_t)w.Wmax);
   w.off_nwork = o;   o = up(o + 4);
+  w.off_split = o;   o = up(o + 4 * (size_t)w.T);
   w.off_entries = o; o = up(o + 16 * (size_t)w.Emax);
   w.bytes = o;
   return w;
@@ -914,38 +959,51 @@ hipError_t launch_forward(const Params &p, DType dt, const LaunchShape &s, hipSt
 hipError_t launch_backward(const Params &p_in, DType dt, const LaunchShape &s, hipStream_t stream) {
   Params p = p_in;
   p.qpb = max(1, 1024 / p.LK);
+  p.lpp = s.lpp;
   // 16-byte grad_out loads in the grad_value pass when rows and pointer allow
   p.gvec = (s.vec * (dt == DType::F32 ? 4 : 2)) == 16 ? 1 : 0;
   hipError_t e;
-  // 1. tile counters
+  // 1. tile counters and the split-tile counter
   {
-    uint32_t *ptr = p.ws.tile_count;  // T counters and the eight work-shard counters
+    uint32_t *ptr = p.ws.tile_count;
     int64_t n = p.T + 8;
     void *args[] = {&ptr, &n};
     e = hipLaunchKernel(reinterpret_cast<const void *>(zero_u32_kernel), dim3((unsigned)((n + kBlock - 1) / kBlock)),
                         dim3(kBlock), args, 0, stream);
     if (e != hipSuccess) return e;
   }
-  // 2. grad_attn, grad_loc
-  if ((e = launch_pairs(false, p, dt, s, stream)) != hipSuccess) return e;
-  // 3. counting sort of (sample, tile) entries
+  // 2. counting sort of (sample, tile) entries; the scatter launch also clears
+  //    the tiles whose grad_value is summed over several work items
   const int64_t bin_blocks = (int64_t)p.N * p.M * ((p.Lq + p.qpb - 1) / p.qpb);
   if ((e = launch_fn(reinterpret_cast<const void *>(bin_kernel<0>), bin_blocks, kBlock, 1, p, stream)) != hipSuccess)
     return e;
   if ((e = launch_fn(reinterpret_cast<const void *>(scan_kernel), 1, 1024, 1, p, stream)) != hipSuccess) return e;
-  if ((e = launch_fn(reinterpret_cast<const void *>(bin_kernel<1>), bin_blocks, kBlock, 1, p, stream)) != hipSuccess)
+  if ((e = launch_fn(reinterpret_cast<const void *>(bin_kernel<1>), bin_blocks + 256, kBlock, 1, p, stream)) !=
+      hipSuccess)
     return e;
-  // 4. grad_value per tile
+  // 3. grad_value per tile, and grad_attn / grad_loc per sample
   const int64_t wmax = p.T + (4 * p.pairs * p.LK + kPartEntries - 1) / kPartEntries;
-  if ((e = launch_fn(reinterpret_cast<const void *>(zero_split_tiles_kernel), std::min<int64_t>(wmax, 1024), kBlock, 1,
-                     p, stream)) != hipSuccess)
-    return e;
   const int Dc = min(kChanGroup, p.D);
   const int cs_need = (Dc + 3) / 4;
   int cs = 1;
   while (cs < cs_need) cs *= 2;
-  KernelFn gv = dt == DType::F32 ? pick_gv<F32>(cs) : pick_gv<BF16>(cs);
   const int groups = (p.D + kChanGroup - 1) / kChanGroup;
+  const int ppb = kBlock / s.lpp;
+  p.pc = min(p.LK, max(1, kDescCap / ppb));
+  const int64_t sample_blocks = (p.pairs + ppb - 1) / ppb;
+  const bool hot_f32 = dt == DType::F32 && s.vec == 4 && s.lpp == 8 && s.ncg == 1 && cs == 8;
+  const bool hot_bf16 = dt == DType::BF16 && s.vec == 8 && s.lpp == 4 && s.ncg == 1 && cs == 8;
+  // grad_value blocks rounded to a multiple of 8 so that the sample blocks'
+  // XCD-aware renumbering sees the hardware's block % 8 placement
+  const int64_t gvb = (wmax + 7) & ~(int64_t)7;
+  if ((hot_f32 || hot_bf16) && groups == 1 && gvb + sample_blocks <= 0x7fffffff) {
+    p.gv_blocks = (int32_t)gvb;
+    const void *fn = hot_f32 ? reinterpret_cast<const void *>(bwd_fused_kernel<F32, 4, 1, 8, 8>)
+                             : reinterpret_cast<const void *>(bwd_fused_kernel<BF16, 8, 1, 4, 8>);
+    return launch_fn(fn, gvb + sample_blocks, kBlock, 1, p, stream);
+  }
+  if ((e = launch_pairs(false, p, dt, s, stream)) != hipSuccess) return e;
+  KernelFn gv = dt == DType::F32 ? pick_gv<F32>(cs) : pick_gv<BF16>(cs);
   return launch_fn(reinterpret_cast<const void *>(gv), wmax, kBlock, groups, p, stream);
 }
 
