@@ -141,11 +141,15 @@ def main():
                            grad_value=s["gv"], grad_loc=s["gl"], grad_attn=s["ga"], workspace=s["ws"])
 
     if args.copy_calibration:
+        # 256 MiB device-to-device copy from a source pushed out of the 256 MB
+        # Infinity Cache by a 1 GiB fill, so its reads and writes go to HBM
         src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        flush = torch.zeros(256 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
+        torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
-        del src, dst
+        del src, dst, flush
 
     for i in range(args.warmup):
         step(sets[i % args.rotate])
