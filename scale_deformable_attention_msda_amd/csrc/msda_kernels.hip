@@ -38,7 +38,7 @@ namespace {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kDescCap = 512;             // sample descriptors staged per chunk
+constexpr int kDescCap = 544;             // sample descriptors staged per chunk (16 x 34)
 constexpr int kRsrcWord3 = 0x00020000;    // gfx9 buffer resource: raw, 32-bit data format
 
 struct F32 {
@@ -170,13 +170,26 @@ struct Sample {
   bool inside;
 };
 
-__device__ __forceinline__ Sample sample_geometry(const Params &p, int64_t P, int pt,
+// Element offset of (image n, row 0, head m, channel 0) for pair P (32-bit:
+// every launch keeps value below 2^28 elements).
+__device__ __forceinline__ uint32_t pair_base(const Params &p, uint32_t P) {
+  const uint32_t lqm = (uint32_t)p.Lq * (uint32_t)p.M;
+  const uint32_t n = P / lqm;
+  const uint32_t m = (P - n * lqm) % (uint32_t)p.M;
+  return (n * (uint32_t)p.S * (uint32_t)p.M + m) * (uint32_t)p.D;
+}
+
+// Exact quotient i / d for i < 1024 and 1 <= d <= 256 with mg = ceil(2^20 / d):
+// the rounding error of mg adds less than 2^-10 to i / d, whose fractional
+// part is 0 or at most 1 - 1/d.
+__device__ __forceinline__ uint32_t small_div(uint32_t i, uint32_t mg) { return (i * mg) >> 20; }
+__device__ __forceinline__ uint32_t small_magic(uint32_t d) { return ((1u << 20) + d - 1) / d; }
+
+__device__ __forceinline__ Sample sample_geometry(const Params &p, uint32_t base_pair, int64_t gi, int l,
                                                   const int32_t *sH, const int32_t *sW,
                                                   const int32_t *sS) {
-  const int64_t gi = P * p.LK + pt;
   const float2 xy = *reinterpret_cast<const float2 *>(p.loc + 2 * gi);
   const float A = p.attn[gi];
-  const int l = pt / p.K;
   const int H = sH[l], W = sW[l], s0 = sS[l];
   float x = fmaf(xy.x, (float)W, -0.5f);
   float y = fmaf(xy.y, (float)H, -0.5f);
@@ -189,16 +202,16 @@ __device__ __forceinline__ Sample sample_geometry(const Params &p, int64_t P, in
   s.b = y - yf;
   s.A = s.inside ? A : 0.0f;
   const int x0 = (int)xf, y0 = (int)yf;
-  const int m = (int)(P % p.M);
-  const int64_t n = P / ((int64_t)p.Lq * p.M);
   const uint32_t row = (uint32_t)p.M * (uint32_t)p.D;
-  const uint32_t base = (uint32_t)(((n * p.S + s0) * p.M + m) * p.D);
+  const uint32_t base = base_pair + (uint32_t)s0 * row;
   const bool xo0 = x0 >= 0, xo1 = x0 + 1 < W, yo0 = y0 >= 0, yo1 = y0 + 1 < H;
   const bool in = s.inside;
-  s.off[0] = (in && yo0 && xo0) ? base + (uint32_t)(y0 * W + x0) * row : kOobElem;
-  s.off[1] = (in && yo0 && xo1) ? base + (uint32_t)(y0 * W + x0 + 1) * row : kOobElem;
-  s.off[2] = (in && yo1 && xo0) ? base + (uint32_t)((y0 + 1) * W + x0) * row : kOobElem;
-  s.off[3] = (in && yo1 && xo1) ? base + (uint32_t)((y0 + 1) * W + x0 + 1) * row : kOobElem;
+  const uint32_t r00 = base + (uint32_t)(y0 * W + x0) * row;
+  const uint32_t rW = (uint32_t)W * row;
+  s.off[0] = (in && yo0 && xo0) ? r00 : kOobElem;
+  s.off[1] = (in && yo0 && xo1) ? r00 + row : kOobElem;
+  s.off[2] = (in && yo1 && xo0) ? r00 + rW : kOobElem;
+  s.off[3] = (in && yo1 && xo1) ? r00 + rW + row : kOobElem;
   return s;
 }
 
@@ -212,17 +225,23 @@ struct __align__(16) FDesc {
 template <typename T, int VEC, int NCG, int LPP>
 __global__ __launch_bounds__(kBlock) void fwd_kernel(const Params p) {
   __shared__ FDesc desc[kDescCap];
+  __shared__ uint32_t pbase[kBlock];
   __shared__ int32_t sH[kMaxLevels], sW[kMaxLevels], sS[kMaxLevels];
   load_levels(p, sH, sW, sS);
 
   const int tid = threadIdx.x;
   const int lpp = LPP > 0 ? LPP : p.lpp;
   const int ppb = kBlock / lpp;
+  // descriptor rows padded by one so that consecutive samples of a pair (the
+  // lanes that write them) fall on different LDS banks
+  const int dstride = ppb + 1;
   const int64_t P0 = (int64_t)xcd_remap(blockIdx.x, gridDim.x) * ppb;
   const int npairs = (int)min((int64_t)ppb, p.pairs - P0);
   const int g = tid / lpp;
   const int j = tid - g * lpp;
   const bool active = g < npairs;
+  if (tid < npairs) pbase[tid] = pair_base(p, (uint32_t)(P0 + tid));
+  const uint32_t kmg = small_magic((uint32_t)p.K);
 
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.value, p.value_elems * (uint32_t)T::size);
   const int nvec = p.D / VEC;
@@ -241,11 +260,14 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(const Params p) {
 
   for (int pc0 = 0; pc0 < p.LK; pc0 += p.pc) {
     const int pcn = min(p.pc, p.LK - pc0);
+    const uint32_t pmg = small_magic((uint32_t)pcn);
     __syncthreads();
     for (int i = tid; i < npairs * pcn; i += kBlock) {
-      const int gg = i / pcn;
+      const int gg = (int)small_div((uint32_t)i, pmg);
       const int pp = i - gg * pcn;
-      const Sample s = sample_geometry(p, P0 + gg, pc0 + pp, sH, sW, sS);
+      const int pt = pc0 + pp;
+      const Sample s = sample_geometry(p, pbase[gg], (P0 + gg) * p.LK + pt, (int)small_div((uint32_t)pt, kmg),
+                                       sH, sW, sS);
       FDesc d;
       const float wa[2] = {1.0f - s.a, s.a};
       const float wb[2] = {1.0f - s.b, s.b};
@@ -255,13 +277,13 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(const Params p) {
         d.off[c] = s.off[c] * (uint32_t)T::size;
         d.w[c] = ok ? s.A * wb[c >> 1] * wa[c & 1] : 0.0f;
       }
-      desc[pp * ppb + gg] = d;
+      desc[pp * dstride + gg] = d;
     }
     __syncthreads();
     if (active) {
 #pragma unroll 2
       for (int pp = 0; pp < pcn; ++pp) {
-        const FDesc d = desc[pp * ppb + g];
+        const FDesc d = desc[pp * dstride + g];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
 #pragma unroll
@@ -309,7 +331,8 @@ struct __align__(16) BDesc {
   float aw, ah;     // attn * W_l, attn * H_l (chain rule through loc * W - 0.5)
 };
 
-constexpr size_t kSampleSmem = kDescCap * sizeof(BDesc) + kDescCap * sizeof(float3) + 3 * kMaxLevels * 4;
+constexpr size_t kSampleSmem =
+    kDescCap * sizeof(BDesc) + kDescCap * sizeof(float3) + 3 * kMaxLevels * 4 + kBlock * 4;
 
 // grad_attn and grad_loc of the pairs of logical block `block` (of `nblocks`),
 // with LDS carved from `smem` (kSampleSmem bytes).
@@ -319,16 +342,20 @@ __device__ __forceinline__ void bwd_sample_body(const Params &p, int block, int 
   float3 *res = reinterpret_cast<float3 *>(smem + kDescCap * sizeof(BDesc));
   int32_t *sH = reinterpret_cast<int32_t *>(smem + kDescCap * (sizeof(BDesc) + sizeof(float3)));
   int32_t *sW = sH + kMaxLevels, *sS = sW + kMaxLevels;
+  uint32_t *pbase = reinterpret_cast<uint32_t *>(sS + kMaxLevels);
   load_levels(p, sH, sW, sS);
 
   const int tid = threadIdx.x;
   const int lpp = LPP > 0 ? LPP : p.lpp;
   const int ppb = kBlock / lpp;
+  const int dstride = ppb + 1;  // padded descriptor rows (see fwd_kernel)
   const int64_t P0 = (int64_t)xcd_remap(block, nblocks) * ppb;
   const int npairs = (int)min((int64_t)ppb, p.pairs - P0);
   const int g = tid / lpp;
   const int j = tid - g * lpp;
   const bool active = g < npairs;
+  if (tid < npairs) pbase[tid] = pair_base(p, (uint32_t)(P0 + tid));
+  const uint32_t kmg = small_magic((uint32_t)p.K);
 
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.value, p.value_elems * (uint32_t)T::size);
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.grad_out, (uint32_t)(p.pairs * p.D) * (uint32_t)T::size);
@@ -345,12 +372,14 @@ __device__ __forceinline__ void bwd_sample_body(const Params &p, int block, int 
 
   for (int pc0 = 0; pc0 < p.LK; pc0 += p.pc) {
     const int pcn = min(p.pc, p.LK - pc0);
+    const uint32_t pmg = small_magic((uint32_t)pcn);
     __syncthreads();
     for (int i = tid; i < npairs * pcn; i += kBlock) {
-      const int gg = i / pcn;
+      const int gg = (int)small_div((uint32_t)i, pmg);
       const int pp = i - gg * pcn;
-      const Sample s = sample_geometry(p, P0 + gg, pc0 + pp, sH, sW, sS);
-      const int l = (pc0 + pp) / p.K;
+      const int pt = pc0 + pp;
+      const int l = (int)small_div((uint32_t)pt, kmg);
+      const Sample s = sample_geometry(p, pbase[gg], (P0 + gg) * p.LK + pt, l, sH, sW, sS);
       BDesc d;
 #pragma unroll
       for (int c = 0; c < 4; ++c) d.off[c] = s.off[c];
@@ -358,12 +387,12 @@ __device__ __forceinline__ void bwd_sample_body(const Params &p, int block, int 
       d.b = s.b;
       d.aw = s.A * (float)sW[l];
       d.ah = s.A * (float)sH[l];
-      desc[pp * ppb + gg] = d;
+      desc[pp * dstride + gg] = d;
     }
     __syncthreads();
     if (active) {
       for (int pp = 0; pp < pcn; ++pp) {
-        const BDesc d = desc[pp * ppb + g];
+        const BDesc d = desc[pp * dstride + g];
         float dot[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -383,14 +412,14 @@ __device__ __forceinline__ void bwd_sample_body(const Params &p, int block, int 
         ga = group_sum<LPP>(ga, lpp);
         gx = group_sum<LPP>(gx, lpp);
         gy = group_sum<LPP>(gy, lpp);
-        if (j == 0) res[pp * ppb + g] = make_float3(ga, d.aw * gx, d.ah * gy);
+        if (j == 0) res[pp * dstride + g] = make_float3(ga, d.aw * gx, d.ah * gy);
       }
     }
     __syncthreads();
     for (int i = tid; i < npairs * pcn; i += kBlock) {
       const int gg = i / pcn;
       const int pp = i - gg * pcn;
-      const float3 r = res[pp * ppb + gg];
+      const float3 r = res[pp * dstride + gg];
       const int64_t gi = (P0 + gg) * p.LK + pc0 + pp;
       p.grad_attn[gi] = r.x;
       *reinterpret_cast<float2 *>(p.grad_loc + 2 * gi) = make_float2(r.y, r.z);
@@ -888,7 +917,7 @@ hipError_t launch_pairs(bool fwd, const Params &p_in, DType dt, const LaunchShap
   Params p = p_in;
   p.lpp = s.lpp;
   const int ppb = kBlock / s.lpp;
-  p.pc = min(p.LK, max(1, kDescCap / ppb));
+  p.pc = min(p.LK, max(1, kDescCap / (ppb + 1)));
   const int64_t blocks = (p.pairs + ppb - 1) / ppb;
   return launch_fn(reinterpret_cast<const void *>(fn), blocks, kBlock, 1, p, stream);
 }
@@ -989,7 +1018,7 @@ hipError_t launch_backward(const Params &p_in, DType dt, const LaunchShape &s, h
   while (cs < cs_need) cs *= 2;
   const int groups = (p.D + kChanGroup - 1) / kChanGroup;
   const int ppb = kBlock / s.lpp;
-  p.pc = min(p.LK, max(1, kDescCap / ppb));
+  p.pc = min(p.LK, max(1, kDescCap / (ppb + 1)));
   const int64_t sample_blocks = (p.pairs + ppb - 1) / ppb;
   const bool hot_f32 = dt == DType::F32 && s.vec == 4 && s.lpp == 8 && s.ncg == 1 && cs == 8;
   const bool hot_bf16 = dt == DType::BF16 && s.vec == 8 && s.lpp == 4 && s.ncg == 1 && cs == 8;
