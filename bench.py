@@ -83,6 +83,65 @@ def cpu_baseline(w, seconds):
             "host_cpus_available": len(os.sched_getaffinity(0))}
 
 
+def decoder_latency(msda, torch, dev, layers=6, reps=20):
+    """Decoder cross-attention shape (N=2, Lq=300, bf16 values): per-layer time of
+    forward+backward issued eagerly vs replayed from one captured HIP graph of
+    `layers` layers (launch overhead is what separates them at this size)."""
+    import numpy as np
+
+    from workloads import config_workload
+
+    w = config_workload("decoder_fwd_bf16", with_grad=True)
+    d = w.dims
+    value = torch.from_numpy(w.value_bits.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+    g = torch.from_numpy(w.grad_out_bits.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+    loc = torch.from_numpy(w.loc).to(dev)
+    attn = torch.from_numpy(w.attn).to(dev)
+    ss, ls = w.spatial_shapes, w.level_start
+    out = torch.empty((d["N"], d["Lq"], d["M"], d["D"]), dtype=torch.bfloat16, device=dev)
+    gv = torch.empty(value.shape, dtype=torch.float32, device=dev)
+    gl = torch.empty_like(loc)
+    ga = torch.empty_like(attn)
+    ws = torch.empty(msda.msda_backward_workspace_size(ss, ls, d["N"], d["S"], d["M"], d["D"], d["L"],
+                                                       d["Lq"], d["K"], msda.MSDA_BF16),
+                     dtype=torch.uint8, device=dev)
+
+    def run(fwd_only=False):
+        for _ in range(layers):
+            msda.msda_forward(value, ss, ls, loc, attn, out=out)
+            if not fwd_only:
+                msda.msda_backward(value, ss, ls, loc, attn, g, grad_value=gv, grad_loc=gl, grad_attn=ga,
+                                   workspace=ws)
+
+    res = {"workload": "decoder cross-attention: N=2, Lq=300, levels 100x167/50x84/25x42/13x21, M=8, "
+                       "D=32, K=4, bf16 values", "layers": layers}
+    for name, fwd_only in (("fwd", True), ("fwd_bwd", False)):
+        run(fwd_only)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            run(fwd_only)
+        torch.cuda.synchronize()
+        eager = (time.perf_counter() - t0) / (reps * layers)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            run(fwd_only)
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run(fwd_only)
+        graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            graph.replay()
+        torch.cuda.synchronize()
+        replay = (time.perf_counter() - t0) / (reps * layers)
+        res[name] = {"eager_us_per_layer": round(eager * 1e6, 2), "graph_us_per_layer": round(replay * 1e6, 2)}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -206,6 +265,7 @@ def main():
         "fwd": fwd, "bwd": bwd,
         "kernel_source_sha256": kernel_source_hash(),
     }
+    result["decoder_latency"] = decoder_latency(msda, torch, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)

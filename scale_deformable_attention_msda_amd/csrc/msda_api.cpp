@@ -100,8 +100,9 @@ msda_status msda_forward(const void *value, const int64_t *spatial_shapes, const
     return MSDA_ERROR_MISALIGNED;
 
   const msda::DType dt = dtype == MSDA_F32 ? msda::DType::F32 : msda::DType::BF16;
-  const msda::LaunchShape shape =
-      msda::choose_shape((int)D, dt, reinterpret_cast<uintptr_t>(value) | reinterpret_cast<uintptr_t>(out));
+  const msda::LaunchShape shape = msda::choose_shape(
+      (int)D, dt, reinterpret_cast<uintptr_t>(value) | reinterpret_cast<uintptr_t>(out),
+      std::min(N, images_per_launch(S, M, D, Lq, L, K)) * Lq * M);
   msda::Params p = base_params(spatial_shapes, level_start, S, M, D, L, Lq, K);
   const int64_t step = images_per_launch(S, M, D, Lq, L, K);
   for (int64_t n0 = 0; n0 < N; n0 += step) {
@@ -159,14 +160,14 @@ msda_status msda_backward(const void *value, const int64_t *spatial_shapes, cons
 
   const msda::DType dt = dtype == MSDA_F32 ? msda::DType::F32 : msda::DType::BF16;
   const msda::LaunchShape shape = msda::choose_shape(
-      (int)D, dt, reinterpret_cast<uintptr_t>(value) | reinterpret_cast<uintptr_t>(grad_out));
+      (int)D, dt, reinterpret_cast<uintptr_t>(value) | reinterpret_cast<uintptr_t>(grad_out),
+      std::min(N, step) * Lq * M);
   msda::Params p = base_params(spatial_shapes, level_start, S, M, D, L, Lq, K);
   char *ws = static_cast<char *>(workspace);
   p.ws.tile_count = reinterpret_cast<uint32_t *>(ws + wl.off_count);
   p.ws.tile_cursor = reinterpret_cast<uint32_t *>(ws + wl.off_cursor);
   p.ws.tile_start = reinterpret_cast<uint32_t *>(ws + wl.off_start);
-  p.ws.work_tile = reinterpret_cast<uint32_t *>(ws + wl.off_wtile);
-  p.ws.work_part = reinterpret_cast<uint32_t *>(ws + wl.off_wpart);
+  p.ws.work_item = reinterpret_cast<uint32_t *>(ws + wl.off_witem);
   p.ws.n_work = reinterpret_cast<uint32_t *>(ws + wl.off_nwork);
   p.ws.split_list = reinterpret_cast<uint32_t *>(ws + wl.off_split);
   p.ws.entries = reinterpret_cast<uint32_t *>(ws + wl.off_entries);

@@ -45,8 +45,7 @@ struct Workspace {
   uint32_t *tile_count;   // [T+8] entries per tile; [T] counts split tiles
   uint32_t *tile_cursor;  // [T]   fill cursor of the scatter pass
   uint32_t *tile_start;   // [T+1] first entry of each tile
-  uint32_t *work_tile;    // [Wmax] work items of the grad_value pass
-  uint32_t *work_part;    // [Wmax]
+  uint32_t *work_item;    // [4*Wmax] grad_value work items {tile, first entry, end entry, split}
   uint32_t *n_work;       // [1]
   uint32_t *split_list;   // [T] tiles whose entries span several work items
   uint32_t *entries;      // [4*Emax] (sample, tile) entries, tile-major, 16-byte records
@@ -73,6 +72,7 @@ struct Params {
   int32_t qpb;           // queries per workgroup of the binning passes
   int32_t gvec;          // grad_out rows allow 16-byte loads
   int32_t gv_blocks;     // grad_value blocks of the fused backward launch
+  int32_t sparse;        // grad_value zero-filled first; empty tiles get no work
   Workspace ws;
   LevelTable lv;
 };
@@ -85,13 +85,15 @@ struct LaunchShape {
   int ncg;   // channel groups per lane
 };
 
-// Picks the lane mapping for a channel count, element type and pointer alignment.
-LaunchShape choose_shape(int D, DType dt, uintptr_t align_bits);
+// Picks the lane mapping for a channel count, element type, pointer alignment
+// and the number of (n, q, m) pairs of the launch.
+LaunchShape choose_shape_widest(int D, DType dt, uintptr_t align_bits);
+LaunchShape choose_shape(int D, DType dt, uintptr_t align_bits, int64_t pairs);
 
 // Tile table and workspace layout of a launch covering `nimg` images.
 struct WorkspaceLayout {
   int64_t T, Wmax, Emax;
-  size_t off_count, off_cursor, off_start, off_wtile, off_wpart, off_nwork, off_split, off_entries, bytes;
+  size_t off_count, off_cursor, off_start, off_witem, off_nwork, off_split, off_entries, bytes;
 };
 WorkspaceLayout workspace_layout(const int64_t *spatial_shapes, int64_t L, int64_t nimg, int64_t M,
                                  int64_t Lq, int64_t K);

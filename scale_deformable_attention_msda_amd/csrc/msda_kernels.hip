@@ -580,46 +580,71 @@ __global__ __launch_bounds__(kBlock) void bin_kernel(const Params p) {
   }
 }
 
-// Exclusive scan of the tile counts (one workgroup of 1024 threads) and the
-// list of grad_value work items: each tile gives max(1, ceil(count /
-// kPartEntries)) items, so every tile, empty or not, is written.
+// Exclusive scan of the tile counts (one workgroup of 1024 threads, each
+// owning a run of consecutive tiles) and the list of grad_value work items:
+// a tile gives ceil(count / kPartEntries) items, at least one unless the
+// launch is sparse (grad_value zero-filled beforehand, empty tiles skipped).
+// Tiles with several items are listed so that they can be zeroed first.
 __global__ __launch_bounds__(1024) void scan_kernel(const Params p) {
   __shared__ uint32_t wsum_c[16], wsum_p[16];
-  __shared__ uint32_t carry[2];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid == 0) carry[0] = carry[1] = 0;
-  __syncthreads();
-  for (int base = 0; base < p.T; base += 1024) {
-    const int t = base + tid;
-    const uint32_t c = t < p.T ? p.ws.tile_count[t] : 0u;
-    const uint32_t parts = t < p.T ? max(1u, (c + kPartEntries - 1) / kPartEntries) : 0u;
-    uint32_t ic = c, ip = parts;
+  const int per = (p.T + 1023) / 1024;
+  const int t0 = tid * per, t1 = min(p.T, t0 + per);
+  auto parts_of = [&](uint32_t c) -> uint32_t {
+    const uint32_t q = (c + kPartEntries - 1) / kPartEntries;
+    return p.sparse ? q : max(1u, q);
+  };
+  uint32_t rc = 0, rp = 0;
+  for (int t = t0; t < t1; ++t) {
+    const uint32_t c = p.ws.tile_count[t];
+    rc += c;
+    rp += parts_of(c);
+  }
+  uint32_t ic = rc, ip = rp;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t yc = __shfl_up(ic, o), yp = __shfl_up(ip, o);
-      if (lane >= o) { ic += yc; ip += yp; }
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t yc = __shfl_up(ic, o), yp = __shfl_up(ip, o);
+    if (lane >= o) {
+      ic += yc;
+      ip += yp;
     }
-    if (lane == 63) { wsum_c[wave] = ic; wsum_p[wave] = ip; }
-    __syncthreads();
-    uint32_t oc = carry[0], op = carry[1];
-    for (int w = 0; w < wave; ++w) { oc += wsum_c[w]; op += wsum_p[w]; }
-    if (t < p.T) {
-      const uint32_t start = oc + ic - c, wb = op + ip - parts;
-      p.ws.tile_start[t] = start;
-      p.ws.tile_cursor[t] = start;
-      if (parts > 1) p.ws.split_list[atomicAdd(p.ws.tile_count + p.T, 1u)] = (uint32_t)t;
-      for (uint32_t k = 0; k < parts; ++k) {
-        p.ws.work_tile[wb + k] = (uint32_t)t;
-        p.ws.work_part[wb + k] = k;
-      }
+  }
+  if (lane == 63) {
+    wsum_c[wave] = ic;
+    wsum_p[wave] = ip;
+  }
+  __syncthreads();
+  uint32_t oc = 0, op = 0, tc = 0, tp = 0;
+#pragma unroll
+  for (int w = 0; w < 16; ++w) {
+    if (w < wave) {
+      oc += wsum_c[w];
+      op += wsum_p[w];
     }
-    __syncthreads();
-    if (tid == 1023) { carry[0] = oc + ic; carry[1] = op + ip; }
-    __syncthreads();
+    tc += wsum_c[w];
+    tp += wsum_p[w];
+  }
+  uint32_t start = oc + ic - rc, wb = op + ip - rp;
+  uint4 *items = reinterpret_cast<uint4 *>(p.ws.work_item);
+  for (int t = t0; t < t1; ++t) {
+    const uint32_t c = p.ws.tile_count[t];
+    const uint32_t parts = parts_of(c);
+    p.ws.tile_start[t] = start;
+    p.ws.tile_cursor[t] = start;
+    if (parts > 1 && !p.sparse) p.ws.split_list[atomicAdd(p.ws.tile_count + p.T, 1u)] = (uint32_t)t;
+    // Items are stored last tile first: each (head, image) block of tiles
+    // ends with the coarse levels, whose crowded tiles then start first.
+    for (uint32_t k = 0; k < parts; ++k) {
+      const uint32_t e0 = start + k * kPartEntries;
+      items[tp - 1 - (wb + k)] = make_uint4((uint32_t)t, e0, min(e0 + (uint32_t)kPartEntries, start + c),
+                                            parts > 1 ? 1u : 0u);
+    }
+    start += c;
+    wb += parts;
   }
   if (tid == 0) {
-    p.ws.tile_start[p.T] = carry[0];
-    *p.ws.n_work = carry[1];
+    p.ws.tile_start[p.T] = tc;
+    *p.ws.n_work = tp;
   }
 }
 
@@ -674,16 +699,16 @@ __device__ __forceinline__ void gv_body(const Params &p, uint32_t bx, int cgroup
   uint32_t *off = cnt + kTilePix;
   int32_t *sH = reinterpret_cast<int32_t *>(off + kTilePix + 1);
   int32_t *sW = sH + kMaxLevels, *sS = sW + kMaxLevels, *sTW = sS + kMaxLevels, *sToff = sTW + kMaxLevels;
+  // the item descriptor and the item count are loaded together (the slot
+  // exists for every block of the grid; past n_work it is ignored)
+  const uint4 item = reinterpret_cast<const uint4 *>(p.ws.work_item)[bx];
   const uint32_t nwork = *p.ws.n_work;
   if (bx >= nwork) return;
-  const uint32_t wi = nwork - 1 - bx;
   load_tile_levels(p, sH, sW, sS, sTW, sToff);
   const int tid = threadIdx.x;
   if (tid < kTilePix) cnt[tid] = 0;
-  const uint32_t t = p.ws.work_tile[wi], part = p.ws.work_part[wi];
-  const uint32_t ea = p.ws.tile_start[t], eb = p.ws.tile_start[t + 1];
-  const bool split = eb - ea > (uint32_t)kPartEntries;
-  const uint32_t e0 = ea + part * kPartEntries, e1 = min(e0 + (uint32_t)kPartEntries, eb);
+  const uint32_t t = item.x, e0 = item.y, e1 = item.z;
+  const bool split = item.w != 0;
   const uint4 *recs = reinterpret_cast<const uint4 *>(p.ws.entries);
   uint4 rec[kEPT];
 #pragma unroll
@@ -924,7 +949,21 @@ hipError_t launch_pairs(bool fwd, const Params &p_in, DType dt, const LaunchShap
 
 }  // namespace
 
-LaunchShape choose_shape(int D, DType dt, uintptr_t align_bits) {
+LaunchShape choose_shape(int D, DType dt, uintptr_t align_bits, int64_t pairs) {
+  LaunchShape s = choose_shape_widest(D, dt, align_bits);
+  // Small launches (decoder-sized): spread the pairs over more workgroups by
+  // giving each lane fewer channels, until there are ~2 workgroups per CU.
+  while (s.vec > 1 && s.ncg == 1 && pairs * s.lpp < 512 * (int64_t)kBlock) {
+    const int vec = s.vec / 2, nvec = D / vec;
+    int lpp = 1;
+    while (lpp < nvec && lpp < 64) lpp *= 2;
+    if (lpp * 1 < nvec) break;  // would need several channel groups per lane
+    s = LaunchShape{vec, lpp, 1};
+  }
+  return s;
+}
+
+LaunchShape choose_shape_widest(int D, DType dt, uintptr_t align_bits) {
   const int esz = dt == DType::F32 ? 4 : 2;
   // Widest access (16, 8, 4, 2 bytes) that divides a head's channels and the
   // pointers' alignment, while one pair fits in 64 lanes x 4 groups.
@@ -966,14 +1005,14 @@ WorkspaceLayout workspace_layout(const int64_t *spatial_shapes, int64_t L, int64
   WorkspaceLayout w{};
   w.T = nimg * M * tpi;
   w.Emax = 4 * nimg * Lq * M * L * K;
-  w.Wmax = w.T + (w.Emax + kPartEntries - 1) / kPartEntries;
+  // grad_value work items, rounded up to the fused launch's block granularity
+  w.Wmax = (w.T + (w.Emax + kPartEntries - 1) / kPartEntries + 7) & ~(int64_t)7;
   auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
   size_t o = 0;
   w.off_count = o;   o = up(o + 4 * (size_t)(w.T + 8));
   w.off_cursor = o;  o = up(o + 4 * (size_t)w.T);
   w.off_start = o;   o = up(o + 4 * (size_t)(w.T + 1));
-  w.off_wtile = o;   o = up(o + 4 * (size_t)w.Wmax);
-  w.off_wpart = o;   o = up(o + 4 * (size_t)w.Wmax);
+  w.off_witem = o;   o = up(o + 16 * (size_t)w.Wmax);
   w.off_nwork = o;   o = up(o + 4);
   w.off_split = o;   o = up(o + 4 * (size_t)w.T);
   w.off_entries = o; o = up(o + 16 * (size_t)w.Emax);
@@ -989,6 +1028,13 @@ hipError_t launch_backward(const Params &p_in, DType dt, const LaunchShape &s, h
   Params p = p_in;
   p.qpb = max(1, 1024 / p.LK);
   p.lpp = s.lpp;
+  // Sparse launches (few samples per value tile, e.g. decoder queries):
+  // zero-fill grad_value once and give work only to tiles with entries.
+  p.sparse = (int64_t)p.Lq * p.LK < 32 * (int64_t)p.TPI ? 1 : 0;
+  if (p.sparse) {
+    hipError_t ez = launch_zero(p.grad_value, (int64_t)p.N * p.S * p.M * p.D, stream);
+    if (ez != hipSuccess) return ez;
+  }
   // 16-byte grad_out loads in the grad_value pass when rows and pointer allow
   p.gvec = (s.vec * (dt == DType::F32 ? 4 : 2)) == 16 ? 1 : 0;
   hipError_t e;
