@@ -4,5 +4,6 @@ TEST INFRASTRUCTURE ONLY: imported by the tests, the smoke check and the
 benchmark's CPU-baseline leg, never by the library or its binding. It shares no
 code with the HIP path.
 """
-from .msda_oracle import (msda_backward, msda_forward, msda_grad_value_rows,  # noqa: F401
-                          pixel_coordinate)
+from .msda_oracle import (fused_locations, msda_backward, msda_forward,  # noqa: F401
+                          msda_fused_backward, msda_fused_forward, msda_grad_value_rows,
+                          pixel_coordinate, softmax_weights)

@@ -237,3 +237,92 @@ def msda_grad_value_rows(value, spatial_shapes, level_start, loc, attn, grad_out
     # Rows requested twice: copy the accumulated value to every duplicate.
     first = np.searchsorted(skeys, keys)
     return res[order[first]]
+
+
+# --- the step before the sampling core ------------------------------------------------------
+#
+# Page "Deformable DETR", section "Deformable attention module": one linear
+# projection of the query gives 2MK offset channels and MK logits, and the
+# logits go through a softmax; section "Multi-scale deformable attention": the
+# weights are normalised jointly over the L*K samples of a head and the
+# sampling location is phi_l(p_hat) + offset, i.e. the reference point in
+# level-l pixels plus an offset in level-l pixels. Section "Variants"
+# (iterative bounding box refinement): with a box as reference, the offsets
+# are scaled by the box's width and height around its centre.
+#
+# Reading R11 (arithmetic of the location, which the pages leave open): the
+# location is formed in binary32, for points as fl(ref + fl(offset / size))
+# with size = W_l for x and H_l for y, and for boxes as one fused
+# multiply-add fl(centre + offset * box_size). It then goes through the same
+# index-coordinate rule as a given location (R1, R3).
+
+
+def softmax_weights(logits):
+    """Softmax over the last two axes (L*K samples of one (n, q, m)), float64."""
+    z = np.asarray(logits, dtype=np.float64)
+    shape = z.shape
+    z = z.reshape(shape[:-2] + (-1,))
+    e = np.exp(z - z.max(axis=-1, keepdims=True))
+    return (e / e.sum(axis=-1, keepdims=True)).reshape(shape)
+
+
+def fused_locations(ref, offsets, spatial_shapes, exact=False):
+    """Normalised locations [N,Lq,M,L,K,2] from reference points ([N,Lq,2]) with
+    offsets in pixels of each level, or from boxes ([N,Lq,4] = cx, cy, w, h)
+    with offsets in units of the box size (reading R11). ``exact=True`` forms
+    them in float64 without binary32 rounding (for finite differences)."""
+    ref = np.asarray(ref)
+    off = np.asarray(offsets)
+    ss = np.asarray(spatial_shapes, dtype=np.int64)
+    L = ss.shape[0]
+    size = np.stack([ss[:, 1], ss[:, 0]], axis=-1)  # (W_l, H_l) per level
+    if exact:
+        off = off.astype(np.float64)
+        r = ref.astype(np.float64)
+        if r.shape[-1] == 2:
+            return r[:, :, None, None, None, :] + off / size.reshape(1, 1, 1, L, 1, 2)
+        return r[:, :, None, None, None, :2] + off * r[:, :, None, None, None, 2:]
+    off = off.astype(np.float32)
+    r = ref.astype(np.float32)
+    if r.shape[-1] == 2:
+        step = (off / size.reshape(1, 1, 1, L, 1, 2).astype(np.float32)).astype(np.float32)
+        return (r[:, :, None, None, None, :] + step).astype(np.float32)
+    # one rounding of centre + offset * size: the float64 product of two
+    # binary32 numbers is exact, the float64 sum rounds at most once more
+    c = r[:, :, None, None, None, :2].astype(np.float64)
+    wh = r[:, :, None, None, None, 2:].astype(np.float64)
+    return (c + off.astype(np.float64) * wh).astype(np.float32)
+
+
+def msda_fused_forward(value, spatial_shapes, level_start, ref, offsets, logits, **kw):
+    """out from the raw step before the core: locations from (ref, offsets),
+    weights = softmax(logits); then the sampling core."""
+    loc = fused_locations(ref, offsets, spatial_shapes, exact=kw.pop("exact_locations", False))
+    return msda_forward(value, spatial_shapes, level_start, loc, softmax_weights(logits), **kw)
+
+
+def msda_fused_backward(value, spatial_shapes, level_start, ref, offsets, logits, grad_out, **kw):
+    """(grad_value, grad_offsets, grad_logits, grad_ref) by the chain rule through
+    the softmax (dA_i/dz_j = A_i (delta_ij - A_j)) and the location formula
+    (d loc / d offset = 1/size for points, box size for boxes; d loc / d ref =
+    identity on the centre, offset on the box size). The rounding of R11 is
+    taken to have derivative 1."""
+    exact = kw.pop("exact_locations", False)
+    loc = fused_locations(ref, offsets, spatial_shapes, exact=exact)
+    A = softmax_weights(logits)
+    gv, gl, ga = msda_backward(value, spatial_shapes, level_start, loc, A, grad_out, **kw)
+    s = (A * ga).sum(axis=(-2, -1), keepdims=True)
+    grad_logits = A * (ga - s)
+    ss = np.asarray(spatial_shapes, dtype=np.int64)
+    L = ss.shape[0]
+    ref64 = np.asarray(ref, dtype=np.float64)
+    if ref64.shape[-1] == 2:
+        size = np.stack([ss[:, 1], ss[:, 0]], axis=-1).reshape(1, 1, 1, L, 1, 2)
+        grad_off = gl / size
+        grad_ref = gl.sum(axis=(2, 3, 4))
+    else:
+        wh = ref64[:, :, None, None, None, 2:]
+        grad_off = gl * wh
+        grad_ref = np.concatenate([gl.sum(axis=(2, 3, 4)),
+                                   (gl * np.asarray(offsets, dtype=np.float64)).sum(axis=(2, 3, 4))], axis=-1)
+    return gv, grad_off, grad_logits, grad_ref

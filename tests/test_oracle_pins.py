@@ -13,7 +13,8 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
-from oracle import msda_backward, msda_forward, msda_grad_value_rows, pixel_coordinate
+from oracle import (fused_locations, msda_backward, msda_forward, msda_fused_backward,
+                    msda_fused_forward, msda_grad_value_rows, pixel_coordinate, softmax_weights)
 from tests.dense_reference import (dense_forward_backward, exact_index_coordinate,
                                    round_fraction_to_f32)
 from workloads import init_pattern_workload, level_starts, uniform_workload
@@ -374,3 +375,84 @@ def test_pair_subset_and_row_subset_agree_with_full():
 def test_level_starts_layout():
     starts, S = level_starts(((100, 167), (50, 84), (25, 42), (13, 21)))
     assert list(starts) == [0, 16700, 20900, 21950] and S == 22223
+
+
+# --- the fused step before the core (softmax of logits, locations from references) -------------
+
+def test_softmax_weights_match_library_softmax():
+    scipy_special = pytest.importorskip("scipy.special")
+    rng = np.random.default_rng(91)
+    z = rng.standard_normal((2, 5, 3, 4, 2)) * 3
+    A = softmax_weights(z)
+    ref = scipy_special.softmax(z.reshape(2, 5, 3, 8), axis=-1).reshape(z.shape)
+    np.testing.assert_allclose(A, ref, atol=1e-15)
+    np.testing.assert_allclose(A.sum(axis=(-2, -1)), 1.0, atol=1e-14)
+    np.testing.assert_allclose(softmax_weights(z + 7.0), A, atol=1e-15)
+
+
+def test_fused_locations_closed_forms():
+    shapes = np.array([[8, 16], [4, 8]])
+    # reference at a pixel centre of level 0 plus an integer pixel offset lands on
+    # a pixel centre of that level
+    ref = np.array([[[(5 + 0.5) / 16, (2 + 0.5) / 8]]], dtype=np.float32)
+    off = np.zeros((1, 1, 1, 2, 1, 2), dtype=np.float32)
+    off[0, 0, 0, 0, 0] = (3.0, -1.0)
+    loc = fused_locations(ref, off, shapes)
+    assert loc[0, 0, 0, 0, 0, 0] * 16 - 0.5 == 8.0 and loc[0, 0, 0, 0, 0, 1] * 8 - 0.5 == 1.0
+    # a zero offset reads the reference point itself at every level
+    np.testing.assert_array_equal(loc[0, 0, 0, 1, 0], ref[0, 0])
+    # boxes: zero offsets give the centre, offset (1, -1) moves by (w, -h)
+    box = np.array([[[0.5, 0.25, 0.125, 0.5]]], dtype=np.float32)
+    offb = np.zeros((1, 1, 1, 1, 2, 2), dtype=np.float32)
+    offb[0, 0, 0, 0, 1] = (1.0, -1.0)
+    locb = fused_locations(box, offb, shapes[:1])
+    np.testing.assert_array_equal(locb[0, 0, 0, 0, 0], [0.5, 0.25])
+    np.testing.assert_array_equal(locb[0, 0, 0, 0, 1], [0.625, -0.25])
+
+
+@pytest.mark.parametrize("ref_dim", [2, 4])
+def test_fused_backward_finite_differences(ref_dim):
+    rng = np.random.default_rng(95 + ref_dim)
+    shapes = np.array([[6, 8], [3, 5]])
+    starts = np.array([0, 48])
+    N, Lq, M, D, L, K = 1, 4, 2, 3, 2, 2
+    value = rng.standard_normal((N, 63, M, D))
+    if ref_dim == 2:
+        ref = rng.uniform(0.1, 0.9, (N, Lq, 2))
+        off = rng.standard_normal((N, Lq, M, L, K, 2)) * 1.5
+    else:
+        ref = np.concatenate([rng.uniform(0.3, 0.7, (N, Lq, 2)), rng.uniform(0.1, 0.4, (N, Lq, 2))], -1)
+        off = rng.uniform(-0.5, 0.5, (N, Lq, M, L, K, 2))
+    logits = rng.standard_normal((N, Lq, M, L, K))
+    G = rng.standard_normal((N, Lq, M, D))
+    kw = dict(round_coords=False, exact_locations=True)
+    _, g_off, g_log, g_ref = msda_fused_backward(value, shapes, starts, ref, off, logits, G, **kw)
+
+    def f(ref=ref, off=off, logits=logits):
+        return (msda_fused_forward(value, shapes, starts, ref, off, logits, **kw) * G).sum()
+
+    h = 1e-6
+    for idx in [(0, 1, 0, 1, 0), (0, 3, 1, 0, 1), (0, 0, 1, 1, 1)]:
+        zp, zm = logits.copy(), logits.copy()
+        zp[idx] += h
+        zm[idx] -= h
+        assert abs((f(logits=zp) - f(logits=zm)) / (2 * h) - g_log[idx]) < 1e-6
+    checked = 0
+    for idx in np.ndindex(*off.shape):
+        op, om = off.copy(), off.copy()
+        op[idx] += h
+        om[idx] -= h
+        fd = (f(off=op) - f(off=om)) / (2 * h)
+        if abs(fd - g_off[idx]) > 1e-5 * max(1.0, abs(fd)):
+            # central differences straddle a kink of the bilinear read
+            x = fused_locations(ref, off, shapes, exact=True)[idx] * shapes[idx[3]][1 - idx[5]] - 0.5
+            assert abs(x - np.round(x)) < 1e-4, (idx, fd, g_off[idx])
+        else:
+            checked += 1
+    assert checked > 40
+    for idx in np.ndindex(*ref.shape):
+        rp, rm = ref.copy(), ref.copy()
+        rp[idx] += h
+        rm[idx] -= h
+        fd = (f(ref=rp) - f(ref=rm)) / (2 * h)
+        assert abs(fd - g_ref[idx]) < 1e-4 * max(1.0, abs(fd)), (idx, fd, g_ref[idx])
