@@ -288,10 +288,29 @@ def fused_locations(ref, offsets, spatial_shapes, exact=False):
         step = (off / size.reshape(1, 1, 1, L, 1, 2).astype(np.float32)).astype(np.float32)
         return (r[:, :, None, None, None, :] + step).astype(np.float32)
     # one rounding of centre + offset * size: the float64 product of two
-    # binary32 numbers is exact, the float64 sum rounds at most once more
+    # binary32 numbers is exact, so only the sum is inexact
     c = r[:, :, None, None, None, :2].astype(np.float64)
     wh = r[:, :, None, None, None, 2:].astype(np.float64)
-    return (c + off.astype(np.float64) * wh).astype(np.float32)
+    return _round_sum_to_f32(np.broadcast_to(c, off.shape), off.astype(np.float64) * wh)
+
+
+def _round_sum_to_f32(a, b):
+    """binary32 nearest (ties to even) of the exact sum of float64 arrays a + b.
+
+    Rounding the float64 sum to binary32 rounds twice; the two differ only when
+    the float64 sum s is exactly halfway between two binary32 numbers while the
+    exact sum is not. Knuth's TwoSum gives the exact error e = (a + b) - s, and
+    its sign then decides the halfway case."""
+    s = a + b
+    bv = s - a
+    e = (a - (s - bv)) + (b - bv)
+    r = s.astype(np.float32)
+    r64 = r.astype(np.float64)
+    other = np.where(r64 > s, np.nextafter(r, np.float32(-np.inf)), np.nextafter(r, np.float32(np.inf)))
+    halfway = (r64 + other.astype(np.float64)) * 0.5 == s
+    # at a halfway s, the exact sum lies on the side of `other` when e points there
+    toward_other = np.sign(e) == np.sign(other.astype(np.float64) - s)
+    return np.where(halfway & (e != 0) & toward_other, other, r).astype(np.float32)
 
 
 def msda_fused_forward(value, spatial_shapes, level_start, ref, offsets, logits, **kw):

@@ -456,3 +456,45 @@ def test_fused_backward_finite_differences(ref_dim):
         rm[idx] -= h
         fd = (f(ref=rp) - f(ref=rm)) / (2 * h)
         assert abs(fd - g_ref[idx]) < 1e-4 * max(1.0, abs(fd)), (idx, fd, g_ref[idx])
+
+
+def test_box_locations_are_one_rounding_of_the_fused_multiply_add():
+    """Reading R11 for boxes: loc = nearest binary32 of centre + offset * size,
+    checked against exact rationals, including inputs where rounding the
+    float64 sum to binary32 would round twice the wrong way."""
+    rng = np.random.default_rng(97)
+    xs, ys = [], []
+    # centre 1, size * offset just above 2^-24: the exact sum lies just above
+    # the binary32 halfway point 1 + 2^-24, its float64 rounding on it
+    for x in rng.uniform(1.0, 2.0, 20000).astype(np.float32):
+        y = np.float32(2.0 ** -24 / float(x))
+        while Fraction(float(x)) * Fraction(float(y)) <= Fraction(1, 2 ** 24):
+            y = np.nextafter(y, np.float32(1))
+        ex = 1 + Fraction(float(x)) * Fraction(float(y))
+        if float(ex) == 1 + 2.0 ** -24:
+            xs.append(x)
+            ys.append(y)
+        if len(xs) == 16:
+            break
+    assert len(xs) == 16
+    n = len(xs)
+    box = np.zeros((1, n, 4), dtype=np.float32)
+    box[0, :, 0] = 1.0
+    box[0, :, 1] = rng.uniform(-1, 1, n)
+    box[0, :, 2] = ys
+    box[0, :, 3] = rng.uniform(0.01, 1, n)
+    off = np.zeros((1, n, 1, 1, 1, 2), dtype=np.float32)
+    off[0, :, 0, 0, 0, 0] = xs
+    off[0, :, 0, 0, 0, 1] = rng.uniform(-3, 3, n)
+    # plus random boxes
+    box2 = rng.uniform(0.0, 1.0, (1, 64, 4)).astype(np.float32)
+    off2 = (rng.standard_normal((1, 64, 1, 1, 1, 2)) * 2).astype(np.float32)
+    shapes = np.array([[4, 4]])
+    for b, o in ((box, off), (box2, off2)):
+        got = fused_locations(b, o, shapes)
+        for q in range(b.shape[1]):
+            for c in range(2):
+                ex = Fraction(float(b[0, q, c])) + Fraction(float(o[0, q, 0, 0, 0, c])) * Fraction(float(b[0, q, 2 + c]))
+                assert got[0, q, 0, 0, 0, c] == round_fraction_to_f32(ex), (q, c)
+    # the halfway cases do round up, away from the float64 sum's tie
+    assert np.all(fused_locations(box, off, shapes)[0, :, 0, 0, 0, 0] == np.float32(1 + 2.0 ** -23))
