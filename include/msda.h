@@ -105,11 +105,12 @@ msda_status msda_forward(const void *value, const int64_t *spatial_shapes,
                          int64_t Lq, int64_t K, int dtype, hipStream_t stream);
 
 /*
- * Bytes of device workspace msda_backward needs for these sizes (the same
- * checks as msda_validate apply). The workspace holds a counting sort of the
- * samples by the 8x8-pixel tile of the value map they touch: a few counters
- * per tile plus up to four 16-byte entries per sample, about 64*N*Lq*M*L*K
- * bytes.
+ * Bytes of device workspace msda_backward and msda_fused_backward need for
+ * these sizes (the same checks as msda_validate apply). The workspace holds a
+ * counting sort of the samples by the 8x8-pixel tile of the value map they
+ * touch: a few counters per tile plus up to four 16-byte entries per sample,
+ * and 24 bytes per (image, query, head) for the fused variant, about
+ * 64*N*Lq*M*L*K + 24*N*Lq*M bytes.
  */
 msda_status msda_backward_workspace_size(const int64_t *spatial_shapes, const int64_t *level_start,
                                          int64_t N, int64_t S, int64_t M, int64_t D, int64_t L,
@@ -139,6 +140,62 @@ msda_status msda_backward(const void *value, const int64_t *spatial_shapes,
                           float *grad_attn, int64_t N, int64_t S, int64_t M, int64_t D,
                           int64_t L, int64_t Lq, int64_t K, int dtype, void *workspace,
                           size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The sampling core with the step in front of it done inside the kernels
+ * (page "Deformable DETR", section "Deformable attention module": the
+ * sampling offsets and the attention logits are one linear projection of the
+ * query, and the logits go through a softmax; section "Multi-scale deformable
+ * attention": the softmax is taken jointly over the L*K samples of a head and
+ * a sample sits at the reference point plus an offset in pixels of level l;
+ * section "Variants", iterative bounding box refinement: with a box as the
+ * reference, the offsets are scaled by the box's width and height). Computes
+ * msda_forward(value, loc, attn) with
+ *   attn[n,q,m,l,k] = softmax over (l, k) of logits[n,q,m,:,:]
+ *   ref_dim == 2 (reference points, normalised (x, y)):
+ *     loc[...,l,k,0] = ref[n,q,0] + offsets[...,l,k,0] / W_l
+ *     loc[...,l,k,1] = ref[n,q,1] + offsets[...,l,k,1] / H_l
+ *     (binary32: the quotient and the sum are each rounded once)
+ *   ref_dim == 4 (boxes (cx, cy, w, h), normalised):
+ *     loc[...,l,k,0] = fmaf(offsets[...,l,k,0], w, cx)
+ *     loc[...,l,k,1] = fmaf(offsets[...,l,k,1], h, cy)
+ * Layouts: ref [N, Lq, ref_dim] float32, device, 8-byte aligned; offsets
+ * [N, Lq, M, L, K, 2] float32 (8-byte aligned); logits [N, Lq, M, L, K]
+ * float32; value and out as for msda_forward. The softmax is evaluated in
+ * float32 as exp(z - max) / sum; a NaN or infinite logit makes its head's
+ * weights NaN. ref_dim other than 2 or 4: MSDA_ERROR_INVALID_VALUE. Other
+ * errors, ownership and asynchrony as for msda_forward.
+ */
+msda_status msda_fused_forward(const void *value, const int64_t *spatial_shapes,
+                               const int64_t *level_start, const float *ref, int ref_dim,
+                               const float *offsets, const float *logits, void *out, int64_t N,
+                               int64_t S, int64_t M, int64_t D, int64_t L, int64_t Lq, int64_t K,
+                               int dtype, hipStream_t stream);
+
+/*
+ * Backward of msda_fused_forward, by the chain rule through the softmax and
+ * the location formula (the rounding of the location is taken to have
+ * derivative 1). With grad_attn and grad_loc as msda_backward defines them:
+ *   grad_logits[i]  = attn[i] * (grad_attn[i] - sum_j attn[j] * grad_attn[j])
+ *                     (j over the L*K samples of the same (n, q, m))
+ *   grad_offsets    = grad_loc / (W_l, H_l)             (ref_dim 2)
+ *                   = grad_loc * (w, h)                 (ref_dim 4)
+ *   grad_ref[n,q,:] = sum over (m, l, k) of grad_loc    (ref_dim 2)
+ *                   = [sum grad_loc, sum grad_loc * offsets]  (ref_dim 4:
+ *                     d/d(cx, cy), then d/d(w, h))
+ * grad_value [N,S,M,D], grad_offsets [N,Lq,M,L,K,2] (8-byte aligned),
+ * grad_logits [N,Lq,M,L,K] and grad_ref [N,Lq,ref_dim] are float32 and
+ * overwritten. grad_ref may be NULL (then it is not computed: reference
+ * points are often detached between layers). Workspace, determinism (all but
+ * grad_value are deterministic), errors and asynchrony as for msda_backward.
+ */
+msda_status msda_fused_backward(const void *value, const int64_t *spatial_shapes,
+                                const int64_t *level_start, const float *ref, int ref_dim,
+                                const float *offsets, const float *logits, const void *grad_out,
+                                float *grad_value, float *grad_offsets, float *grad_logits,
+                                float *grad_ref, int64_t N, int64_t S, int64_t M, int64_t D,
+                                int64_t L, int64_t Lq, int64_t K, int dtype, void *workspace,
+                                size_t workspace_bytes, hipStream_t stream);
 
 /* Static description of a status code; never NULL. */
 const char *msda_status_string(msda_status status);

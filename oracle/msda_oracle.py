@@ -320,28 +320,46 @@ def msda_fused_forward(value, spatial_shapes, level_start, ref, offsets, logits,
     return msda_forward(value, spatial_shapes, level_start, loc, softmax_weights(logits), **kw)
 
 
-def msda_fused_backward(value, spatial_shapes, level_start, ref, offsets, logits, grad_out, **kw):
+def msda_fused_backward(value, spatial_shapes, level_start, ref, offsets, logits, grad_out, queries=None,
+                        **kw):
     """(grad_value, grad_offsets, grad_logits, grad_ref) by the chain rule through
     the softmax (dA_i/dz_j = A_i (delta_ij - A_j)) and the location formula
     (d loc / d offset = 1/size for points, box size for boxes; d loc / d ref =
     identity on the centre, offset on the box size). The rounding of R11 is
-    taken to have derivative 1."""
+    taken to have derivative 1.
+
+    ``queries=(n, q)`` restricts the result to the listed queries (all M heads
+    of each): grad_value is then None and the other three are [Q, M, L, K, 2],
+    [Q, M, L, K] and [Q, ref_dim]."""
     exact = kw.pop("exact_locations", False)
     loc = fused_locations(ref, offsets, spatial_shapes, exact=exact)
     A = softmax_weights(logits)
-    gv, gl, ga = msda_backward(value, spatial_shapes, level_start, loc, A, grad_out, **kw)
+    off = np.asarray(offsets, dtype=np.float64)
+    ref64 = np.asarray(ref, dtype=np.float64)
+    if queries is None:
+        gv, gl, ga = msda_backward(value, spatial_shapes, level_start, loc, A, grad_out, **kw)
+    else:
+        qn, qq = (np.asarray(a, dtype=np.int64) for a in queries)
+        Q, M = len(qn), off.shape[2]
+        pairs = (np.repeat(qn, M), np.repeat(qq, M), np.tile(np.arange(M), Q))
+        gv, gl, ga = msda_backward(value, spatial_shapes, level_start, loc, A, grad_out, pairs=pairs,
+                                   with_grad_value=False, **kw)
+        gl = gl.reshape((Q,) + off.shape[2:])
+        ga = ga.reshape((Q,) + off.shape[2:5])
+        A, off, ref64 = A[qn, qq], off[qn, qq], ref64[qn, qq]
+    # from here on the arrays are [..., M, L, K(, 2)] behind the query axes
     s = (A * ga).sum(axis=(-2, -1), keepdims=True)
     grad_logits = A * (ga - s)
     ss = np.asarray(spatial_shapes, dtype=np.int64)
     L = ss.shape[0]
-    ref64 = np.asarray(ref, dtype=np.float64)
+    heads_levels_points = (-4, -3, -2)
     if ref64.shape[-1] == 2:
-        size = np.stack([ss[:, 1], ss[:, 0]], axis=-1).reshape(1, 1, 1, L, 1, 2)
+        size = np.stack([ss[:, 1], ss[:, 0]], axis=-1).reshape(L, 1, 2)  # (W_l, H_l)
         grad_off = gl / size
-        grad_ref = gl.sum(axis=(2, 3, 4))
+        grad_ref = gl.sum(axis=heads_levels_points)
     else:
-        wh = ref64[:, :, None, None, None, 2:]
+        wh = ref64[..., None, None, None, 2:]
         grad_off = gl * wh
-        grad_ref = np.concatenate([gl.sum(axis=(2, 3, 4)),
-                                   (gl * np.asarray(offsets, dtype=np.float64)).sum(axis=(2, 3, 4))], axis=-1)
+        grad_ref = np.concatenate([gl.sum(axis=heads_levels_points),
+                                   (gl * off).sum(axis=heads_levels_points)], axis=-1)
     return gv, grad_off, grad_logits, grad_ref

@@ -52,6 +52,10 @@ def load_library():
     lib.msda_backward.restype = ci
     lib.msda_backward_workspace_size.argtypes = [vp, vp] + [i64] * 7 + [ci, ctypes.POINTER(ctypes.c_size_t)]
     lib.msda_backward_workspace_size.restype = ci
+    lib.msda_fused_forward.argtypes = [vp] * 4 + [ci] + [vp] * 3 + [i64] * 7 + [ci, vp]
+    lib.msda_fused_forward.restype = ci
+    lib.msda_fused_backward.argtypes = [vp] * 4 + [ci] + [vp] * 7 + [i64] * 7 + [ci, vp, ctypes.c_size_t, vp]
+    lib.msda_fused_backward.restype = ci
     lib.msda_status_string.argtypes = [ci]
     lib.msda_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -194,6 +198,93 @@ def msda_backward(value, spatial_shapes, level_start, loc, attn, grad_out, grad_
     return grad_value, grad_loc, grad_attn
 
 
+def _fused_dims(value, ref, offsets, logits):
+    if value.dim() != 4 or ref.dim() != 3 or offsets.dim() != 6 or logits.dim() != 5:
+        raise ValueError("expected value [N,S,M,D], ref [N,Lq,2|4], offsets [N,Lq,M,L,K,2], "
+                         "logits [N,Lq,M,L,K]")
+    N, S, M, D = value.shape
+    N2, Lq, M2, L, K, two = offsets.shape
+    if (N2, M2, two) != (N, M, 2) or tuple(logits.shape) != (N, Lq, M, L, K) or \
+            tuple(ref.shape[:2]) != (N, Lq) or ref.shape[2] not in (2, 4):
+        raise ValueError(f"shape mismatch: value {tuple(value.shape)}, ref {tuple(ref.shape)}, "
+                         f"offsets {tuple(offsets.shape)}, logits {tuple(logits.shape)}")
+    return N, S, M, D, L, Lq, K, int(ref.shape[2])
+
+
+def msda_fused_forward(value, spatial_shapes, level_start, ref, offsets, logits, out=None, stream=None):
+    """out[N,Lq,M,D] from raw predictions: attn = softmax of logits over (L, K),
+    loc = reference point + offsets / (W_l, H_l) (ref [N,Lq,2]) or box centre +
+    offsets * (w, h) (ref [N,Lq,4] = cx, cy, w, h), then the sampling core."""
+    lib = load_library()
+    _device_tensor(value, "value")
+    dt = _dtype_code(value.dtype)
+    for t, name in ((ref, "ref"), (offsets, "offsets"), (logits, "logits")):
+        _device_tensor(t, name, torch.float32)
+    N, S, M, D, L, Lq, K, rd = _fused_dims(value, ref, offsets, logits)
+    ss = _host_i64(spatial_shapes, (L, 2), "spatial_shapes")
+    ls = _host_i64(level_start, (L,), "level_start")
+    if out is None:
+        out = torch.empty((N, Lq, M, D), dtype=value.dtype, device=value.device)
+    else:
+        _device_tensor(out, "out", value.dtype)
+        if tuple(out.shape) != (N, Lq, M, D):
+            raise ValueError(f"out must be {(N, Lq, M, D)}")
+    with torch.cuda.device(value.device):
+        s = torch.cuda.current_stream().cuda_stream if stream is None else int(stream)
+        _raise(lib.msda_fused_forward(value.data_ptr(), ss.ctypes.data, ls.ctypes.data, ref.data_ptr(), rd,
+                                      offsets.data_ptr(), logits.data_ptr(), out.data_ptr(), N, S, M, D, L,
+                                      Lq, K, dt, s))
+    return out
+
+
+def msda_fused_backward(value, spatial_shapes, level_start, ref, offsets, logits, grad_out, grad_value=None,
+                        grad_offsets=None, grad_logits=None, grad_ref=None, need_grad_ref=True,
+                        workspace=None, stream=None):
+    """(grad_value, grad_offsets, grad_logits, grad_ref or None), float32, of
+    msda_fused_forward. ``need_grad_ref=False`` skips the reference gradient."""
+    lib = load_library()
+    _device_tensor(value, "value")
+    dt = _dtype_code(value.dtype)
+    for t, name in ((ref, "ref"), (offsets, "offsets"), (logits, "logits")):
+        _device_tensor(t, name, torch.float32)
+    _device_tensor(grad_out, "grad_out", value.dtype)
+    N, S, M, D, L, Lq, K, rd = _fused_dims(value, ref, offsets, logits)
+    if tuple(grad_out.shape) != (N, Lq, M, D):
+        raise ValueError(f"grad_out must be {(N, Lq, M, D)}")
+    ss = _host_i64(spatial_shapes, (L, 2), "spatial_shapes")
+    ls = _host_i64(level_start, (L,), "level_start")
+    dev = value.device
+    if grad_value is None:
+        grad_value = torch.empty((N, S, M, D), dtype=torch.float32, device=dev)
+    if grad_offsets is None:
+        grad_offsets = torch.empty((N, Lq, M, L, K, 2), dtype=torch.float32, device=dev)
+    if grad_logits is None:
+        grad_logits = torch.empty((N, Lq, M, L, K), dtype=torch.float32, device=dev)
+    if grad_ref is None and need_grad_ref:
+        grad_ref = torch.empty((N, Lq, rd), dtype=torch.float32, device=dev)
+    outs = [(grad_value, "grad_value", (N, S, M, D)), (grad_offsets, "grad_offsets", (N, Lq, M, L, K, 2)),
+            (grad_logits, "grad_logits", (N, Lq, M, L, K))]
+    if grad_ref is not None:
+        outs.append((grad_ref, "grad_ref", (N, Lq, rd)))
+    for t, name, shape in outs:
+        _device_tensor(t, name, torch.float32)
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be {shape}")
+    need = msda_backward_workspace_size(ss, ls, N, S, M, D, L, Lq, K, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    else:
+        _device_tensor(workspace, "workspace", torch.uint8)
+    with torch.cuda.device(dev):
+        s = torch.cuda.current_stream().cuda_stream if stream is None else int(stream)
+        _raise(lib.msda_fused_backward(value.data_ptr(), ss.ctypes.data, ls.ctypes.data, ref.data_ptr(), rd,
+                                       offsets.data_ptr(), logits.data_ptr(), grad_out.data_ptr(),
+                                       grad_value.data_ptr(), grad_offsets.data_ptr(), grad_logits.data_ptr(),
+                                       grad_ref.data_ptr() if grad_ref is not None else None,
+                                       N, S, M, D, L, Lq, K, dt, workspace.data_ptr(), workspace.numel(), s))
+    return grad_value, grad_offsets, grad_logits, grad_ref
+
+
 class MSDeformAttnSampling(torch.autograd.Function):
     """Autograd wrapper: forward and backward both run in libmsda.so."""
 
@@ -216,3 +307,29 @@ class MSDeformAttnSampling(torch.autograd.Function):
 def msda_sample(value, spatial_shapes, level_start, loc, attn):
     """Differentiable sampling core (value, loc and attn receive gradients)."""
     return MSDeformAttnSampling.apply(value, spatial_shapes, level_start, loc, attn)
+
+
+class MSDeformAttnFused(torch.autograd.Function):
+    """Autograd wrapper of the fused entry points (value, ref, offsets and
+    logits receive gradients)."""
+
+    @staticmethod
+    def forward(ctx, value, spatial_shapes, level_start, ref, offsets, logits):
+        ss = _host_i64(spatial_shapes, (offsets.shape[3], 2), "spatial_shapes")
+        ls = _host_i64(level_start, (offsets.shape[3],), "level_start")
+        ctx.save_for_backward(value, ref, offsets, logits)
+        ctx.levels = (ss, ls)
+        return msda_fused_forward(value, ss, ls, ref, offsets, logits)
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        value, ref, offsets, logits = ctx.saved_tensors
+        ss, ls = ctx.levels
+        gv, go, gz, gr = msda_fused_backward(value, ss, ls, ref, offsets, logits, grad_out.contiguous(),
+                                             need_grad_ref=ctx.needs_input_grad[3])
+        return gv.to(value.dtype), None, None, gr, go, gz
+
+
+def msda_fused_sample(value, spatial_shapes, level_start, ref, offsets, logits):
+    """Differentiable sampling core fed by raw offsets and logits."""
+    return MSDeformAttnFused.apply(value, spatial_shapes, level_start, ref, offsets, logits)

@@ -50,6 +50,109 @@ bool levels_cover_all_rows(const int64_t *spatial_shapes, int64_t L, int64_t S) 
   return covered == S;  // levels are disjoint (checked), so this means no gap
 }
 
+msda_status forward_impl(const void *value, const int64_t *spatial_shapes, const int64_t *level_start,
+                         const float *loc, const float *attn, const float *ref, int ref_dim, void *out, int64_t N,
+                         int64_t S, int64_t M, int64_t D, int64_t L, int64_t Lq, int64_t K, int dtype,
+                         hipStream_t stream) {
+  msda_status st = msda_validate(spatial_shapes, level_start, N, S, M, D, L, Lq, K, dtype);
+  if (st != MSDA_SUCCESS) return st;
+  if (ref_dim != 0 && ref_dim != 2 && ref_dim != 4) return MSDA_ERROR_INVALID_VALUE;
+  if (N == 0 || Lq == 0) return MSDA_SUCCESS;
+  if (!value || !loc || !attn || !out || (ref_dim && !ref)) return MSDA_ERROR_INVALID_VALUE;
+  const int64_t esz = elem_size(dtype);
+  if (!aligned(value, esz) || !aligned(out, esz) || !aligned(loc, 8) || !aligned(attn, 4) ||
+      (ref_dim && !aligned(ref, 8)))
+    return MSDA_ERROR_MISALIGNED;
+
+  const msda::DType dt = dtype == MSDA_F32 ? msda::DType::F32 : msda::DType::BF16;
+  const msda::LaunchShape shape = msda::choose_shape(
+      (int)D, dt, reinterpret_cast<uintptr_t>(value) | reinterpret_cast<uintptr_t>(out),
+      std::min(N, images_per_launch(S, M, D, Lq, L, K)) * Lq * M);
+  msda::Params p = base_params(spatial_shapes, level_start, S, M, D, L, Lq, K);
+  p.ref_dim = ref_dim;
+  const int64_t step = images_per_launch(S, M, D, Lq, L, K);
+  for (int64_t n0 = 0; n0 < N; n0 += step) {
+    const int64_t nb = std::min(step, N - n0);
+    p.N = (int32_t)nb;
+    p.pairs = nb * Lq * M;
+    p.value_elems = (uint32_t)(nb * S * M * D);
+    p.value = static_cast<const char *>(value) + n0 * S * M * D * esz;
+    p.loc = loc + n0 * Lq * M * L * K * 2;
+    p.attn = attn + n0 * Lq * M * L * K;
+    p.ref = ref_dim ? ref + n0 * Lq * ref_dim : nullptr;
+    p.out = static_cast<char *>(out) + n0 * Lq * M * D * esz;
+    if (msda::launch_forward(p, dt, shape, stream) != hipSuccess) return MSDA_ERROR_LAUNCH;
+  }
+  return MSDA_SUCCESS;
+}
+
+msda_status backward_impl(const void *value, const int64_t *spatial_shapes, const int64_t *level_start,
+                          const float *loc, const float *attn, const float *ref, int ref_dim, const void *grad_out,
+                          float *grad_value, float *grad_loc, float *grad_attn, float *grad_ref, int64_t N,
+                          int64_t S, int64_t M, int64_t D, int64_t L, int64_t Lq, int64_t K, int dtype,
+                          void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  msda_status st = msda_validate(spatial_shapes, level_start, N, S, M, D, L, Lq, K, dtype);
+  if (st != MSDA_SUCCESS) return st;
+  if (ref_dim != 0 && ref_dim != 2 && ref_dim != 4) return MSDA_ERROR_INVALID_VALUE;
+  if (N == 0) return MSDA_SUCCESS;
+  if (!grad_value) return MSDA_ERROR_INVALID_VALUE;
+  if (!aligned(grad_value, 4)) return MSDA_ERROR_MISALIGNED;
+  const int64_t esz = elem_size(dtype);
+  const int64_t step = images_per_launch(S, M, D, Lq, L, K);
+  const msda::WorkspaceLayout wl = msda::workspace_layout(spatial_shapes, L, std::min(step, N), M, Lq, K);
+  if (Lq > 0) {
+    if (!value || !loc || !attn || !grad_out || !grad_loc || !grad_attn || (ref_dim && !ref))
+      return MSDA_ERROR_INVALID_VALUE;
+    if (!aligned(value, esz) || !aligned(grad_out, esz) || !aligned(loc, 8) || !aligned(attn, 4) ||
+        !aligned(grad_loc, 8) || !aligned(grad_attn, 4) || (ref_dim && !aligned(ref, 8)) ||
+        (grad_ref && !aligned(grad_ref, 4)))
+      return MSDA_ERROR_MISALIGNED;
+    if (!workspace || workspace_bytes < wl.bytes) return MSDA_ERROR_WORKSPACE;
+    if (!aligned(workspace, 256)) return MSDA_ERROR_MISALIGNED;
+  }
+  // Rows outside every level (or every row when there are no queries) get
+  // no tile owner: zero them in full first.
+  if (Lq == 0 || !levels_cover_all_rows(spatial_shapes, L, S)) {
+    if (msda::launch_zero(grad_value, N * S * M * D, stream) != hipSuccess) return MSDA_ERROR_LAUNCH;
+  }
+  if (Lq == 0) return MSDA_SUCCESS;
+
+  const msda::DType dt = dtype == MSDA_F32 ? msda::DType::F32 : msda::DType::BF16;
+  const msda::LaunchShape shape = msda::choose_shape(
+      (int)D, dt, reinterpret_cast<uintptr_t>(value) | reinterpret_cast<uintptr_t>(grad_out),
+      std::min(N, step) * Lq * M);
+  msda::Params p = base_params(spatial_shapes, level_start, S, M, D, L, Lq, K);
+  p.ref_dim = ref_dim;
+  char *ws = static_cast<char *>(workspace);
+  p.ws.tile_count = reinterpret_cast<uint32_t *>(ws + wl.off_count);
+  p.ws.tile_cursor = reinterpret_cast<uint32_t *>(ws + wl.off_cursor);
+  p.ws.tile_start = reinterpret_cast<uint32_t *>(ws + wl.off_start);
+  p.ws.work_item = reinterpret_cast<uint32_t *>(ws + wl.off_witem);
+  p.ws.n_work = reinterpret_cast<uint32_t *>(ws + wl.off_nwork);
+  p.ws.split_list = reinterpret_cast<uint32_t *>(ws + wl.off_split);
+  p.ws.entries = reinterpret_cast<uint32_t *>(ws + wl.off_entries);
+  p.ws.stats = reinterpret_cast<float *>(ws + wl.off_stats);
+  p.ws.ref_part = reinterpret_cast<float *>(ws + wl.off_refpart);
+  for (int64_t n0 = 0; n0 < N; n0 += step) {
+    const int64_t nb = std::min(step, N - n0);
+    p.N = (int32_t)nb;
+    p.pairs = nb * Lq * M;
+    p.T = (int32_t)(nb * M * p.TPI);
+    p.value_elems = (uint32_t)(nb * S * M * D);
+    p.value = static_cast<const char *>(value) + n0 * S * M * D * esz;
+    p.loc = loc + n0 * Lq * M * L * K * 2;
+    p.attn = attn + n0 * Lq * M * L * K;
+    p.ref = ref_dim ? ref + n0 * Lq * ref_dim : nullptr;
+    p.grad_out = static_cast<const char *>(grad_out) + n0 * Lq * M * D * esz;
+    p.grad_value = grad_value + n0 * S * M * D;
+    p.grad_loc = grad_loc + n0 * Lq * M * L * K * 2;
+    p.grad_attn = grad_attn + n0 * Lq * M * L * K;
+    p.grad_ref = (ref_dim && grad_ref) ? grad_ref + n0 * Lq * ref_dim : nullptr;
+    if (msda::launch_backward(p, dt, shape, stream) != hipSuccess) return MSDA_ERROR_LAUNCH;
+  }
+  return MSDA_SUCCESS;
+}
+
 }  // namespace
 
 extern "C" {
@@ -91,32 +194,17 @@ msda_status msda_validate(const int64_t *spatial_shapes, const int64_t *level_st
 msda_status msda_forward(const void *value, const int64_t *spatial_shapes, const int64_t *level_start,
                          const float *loc, const float *attn, void *out, int64_t N, int64_t S, int64_t M,
                          int64_t D, int64_t L, int64_t Lq, int64_t K, int dtype, hipStream_t stream) {
-  msda_status st = msda_validate(spatial_shapes, level_start, N, S, M, D, L, Lq, K, dtype);
-  if (st != MSDA_SUCCESS) return st;
-  if (N == 0 || Lq == 0) return MSDA_SUCCESS;
-  if (!value || !loc || !attn || !out) return MSDA_ERROR_INVALID_VALUE;
-  const int64_t esz = elem_size(dtype);
-  if (!aligned(value, esz) || !aligned(out, esz) || !aligned(loc, 8) || !aligned(attn, 4))
-    return MSDA_ERROR_MISALIGNED;
+  return forward_impl(value, spatial_shapes, level_start, loc, attn, nullptr, 0, out, N, S, M, D, L, Lq, K, dtype,
+                      stream);
+}
 
-  const msda::DType dt = dtype == MSDA_F32 ? msda::DType::F32 : msda::DType::BF16;
-  const msda::LaunchShape shape = msda::choose_shape(
-      (int)D, dt, reinterpret_cast<uintptr_t>(value) | reinterpret_cast<uintptr_t>(out),
-      std::min(N, images_per_launch(S, M, D, Lq, L, K)) * Lq * M);
-  msda::Params p = base_params(spatial_shapes, level_start, S, M, D, L, Lq, K);
-  const int64_t step = images_per_launch(S, M, D, Lq, L, K);
-  for (int64_t n0 = 0; n0 < N; n0 += step) {
-    const int64_t nb = std::min(step, N - n0);
-    p.N = (int32_t)nb;
-    p.pairs = nb * Lq * M;
-    p.value_elems = (uint32_t)(nb * S * M * D);
-    p.value = static_cast<const char *>(value) + n0 * S * M * D * esz;
-    p.loc = loc + n0 * Lq * M * L * K * 2;
-    p.attn = attn + n0 * Lq * M * L * K;
-    p.out = static_cast<char *>(out) + n0 * Lq * M * D * esz;
-    if (msda::launch_forward(p, dt, shape, stream) != hipSuccess) return MSDA_ERROR_LAUNCH;
-  }
-  return MSDA_SUCCESS;
+msda_status msda_fused_forward(const void *value, const int64_t *spatial_shapes, const int64_t *level_start,
+                               const float *ref, int ref_dim, const float *offsets, const float *logits, void *out,
+                               int64_t N, int64_t S, int64_t M, int64_t D, int64_t L, int64_t Lq, int64_t K,
+                               int dtype, hipStream_t stream) {
+  if (ref_dim != 2 && ref_dim != 4) return MSDA_ERROR_INVALID_VALUE;
+  return forward_impl(value, spatial_shapes, level_start, offsets, logits, ref, ref_dim, out, N, S, M, D, L, Lq, K,
+                      dtype, stream);
 }
 
 msda_status msda_backward_workspace_size(const int64_t *spatial_shapes, const int64_t *level_start, int64_t N,
@@ -135,58 +223,20 @@ msda_status msda_backward(const void *value, const int64_t *spatial_shapes, cons
                           float *grad_loc, float *grad_attn, int64_t N, int64_t S, int64_t M, int64_t D,
                           int64_t L, int64_t Lq, int64_t K, int dtype, void *workspace, size_t workspace_bytes,
                           hipStream_t stream) {
-  msda_status st = msda_validate(spatial_shapes, level_start, N, S, M, D, L, Lq, K, dtype);
-  if (st != MSDA_SUCCESS) return st;
-  if (N == 0) return MSDA_SUCCESS;
-  if (!grad_value) return MSDA_ERROR_INVALID_VALUE;
-  if (!aligned(grad_value, 4)) return MSDA_ERROR_MISALIGNED;
-  const int64_t esz = elem_size(dtype);
-  const int64_t step = images_per_launch(S, M, D, Lq, L, K);
-  const msda::WorkspaceLayout wl = msda::workspace_layout(spatial_shapes, L, std::min(step, N), M, Lq, K);
-  if (Lq > 0) {
-    if (!value || !loc || !attn || !grad_out || !grad_loc || !grad_attn) return MSDA_ERROR_INVALID_VALUE;
-    if (!aligned(value, esz) || !aligned(grad_out, esz) || !aligned(loc, 8) || !aligned(attn, 4) ||
-        !aligned(grad_loc, 8) || !aligned(grad_attn, 4))
-      return MSDA_ERROR_MISALIGNED;
-    if (!workspace || workspace_bytes < wl.bytes) return MSDA_ERROR_WORKSPACE;
-    if (!aligned(workspace, 256)) return MSDA_ERROR_MISALIGNED;
-  }
-  // Rows outside every level (or every row when there are no queries) get
-  // no tile owner: zero them in full first.
-  if (Lq == 0 || !levels_cover_all_rows(spatial_shapes, L, S)) {
-    if (msda::launch_zero(grad_value, N * S * M * D, stream) != hipSuccess) return MSDA_ERROR_LAUNCH;
-  }
-  if (Lq == 0) return MSDA_SUCCESS;
+  return backward_impl(value, spatial_shapes, level_start, loc, attn, nullptr, 0, grad_out, grad_value, grad_loc,
+                       grad_attn, nullptr, N, S, M, D, L, Lq, K, dtype, workspace, workspace_bytes, stream);
+}
 
-  const msda::DType dt = dtype == MSDA_F32 ? msda::DType::F32 : msda::DType::BF16;
-  const msda::LaunchShape shape = msda::choose_shape(
-      (int)D, dt, reinterpret_cast<uintptr_t>(value) | reinterpret_cast<uintptr_t>(grad_out),
-      std::min(N, step) * Lq * M);
-  msda::Params p = base_params(spatial_shapes, level_start, S, M, D, L, Lq, K);
-  char *ws = static_cast<char *>(workspace);
-  p.ws.tile_count = reinterpret_cast<uint32_t *>(ws + wl.off_count);
-  p.ws.tile_cursor = reinterpret_cast<uint32_t *>(ws + wl.off_cursor);
-  p.ws.tile_start = reinterpret_cast<uint32_t *>(ws + wl.off_start);
-  p.ws.work_item = reinterpret_cast<uint32_t *>(ws + wl.off_witem);
-  p.ws.n_work = reinterpret_cast<uint32_t *>(ws + wl.off_nwork);
-  p.ws.split_list = reinterpret_cast<uint32_t *>(ws + wl.off_split);
-  p.ws.entries = reinterpret_cast<uint32_t *>(ws + wl.off_entries);
-  for (int64_t n0 = 0; n0 < N; n0 += step) {
-    const int64_t nb = std::min(step, N - n0);
-    p.N = (int32_t)nb;
-    p.pairs = nb * Lq * M;
-    p.T = (int32_t)(nb * M * p.TPI);
-    p.value_elems = (uint32_t)(nb * S * M * D);
-    p.value = static_cast<const char *>(value) + n0 * S * M * D * esz;
-    p.loc = loc + n0 * Lq * M * L * K * 2;
-    p.attn = attn + n0 * Lq * M * L * K;
-    p.grad_out = static_cast<const char *>(grad_out) + n0 * Lq * M * D * esz;
-    p.grad_value = grad_value + n0 * S * M * D;
-    p.grad_loc = grad_loc + n0 * Lq * M * L * K * 2;
-    p.grad_attn = grad_attn + n0 * Lq * M * L * K;
-    if (msda::launch_backward(p, dt, shape, stream) != hipSuccess) return MSDA_ERROR_LAUNCH;
-  }
-  return MSDA_SUCCESS;
+msda_status msda_fused_backward(const void *value, const int64_t *spatial_shapes, const int64_t *level_start,
+                                const float *ref, int ref_dim, const float *offsets, const float *logits,
+                                const void *grad_out, float *grad_value, float *grad_offsets, float *grad_logits,
+                                float *grad_ref, int64_t N, int64_t S, int64_t M, int64_t D, int64_t L, int64_t Lq,
+                                int64_t K, int dtype, void *workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  if (ref_dim != 2 && ref_dim != 4) return MSDA_ERROR_INVALID_VALUE;
+  return backward_impl(value, spatial_shapes, level_start, offsets, logits, ref, ref_dim, grad_out, grad_value,
+                       grad_offsets, grad_logits, grad_ref, N, S, M, D, L, Lq, K, dtype, workspace,
+                       workspace_bytes, stream);
 }
 
 const char *msda_status_string(msda_status status) {

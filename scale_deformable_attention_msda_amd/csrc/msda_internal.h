@@ -49,6 +49,8 @@ struct Workspace {
   uint32_t *n_work;       // [1]
   uint32_t *split_list;   // [T] tiles whose entries span several work items
   uint32_t *entries;      // [4*Emax] (sample, tile) entries, tile-major, 16-byte records
+  float *stats;           // [2*pairs] softmax max and 1/sum of each pair's logits (fused inputs)
+  float *ref_part;        // [4*pairs] per-pair sums of the reference gradient (fused inputs)
 };
 
 // One launch covers images [0, N) of the pointers below (the host offsets the
@@ -73,6 +75,12 @@ struct Params {
   int32_t gvec;          // grad_out rows allow 16-byte loads
   int32_t gv_blocks;     // grad_value blocks of the fused backward launch
   int32_t sparse;        // grad_value zero-filled first; empty tiles get no work
+  // Fused inputs (ref_dim 2 or 4): loc then holds offsets, attn holds logits,
+  // and grad_loc / grad_attn receive the offset and logit gradients.
+  // ref_dim 0: loc and attn are the sampling core's own inputs.
+  const float *ref;      // [pairs / M, ref_dim] reference points or boxes
+  int32_t ref_dim;
+  float *grad_ref;       // [pairs / M, ref_dim], may be null
   Workspace ws;
   LevelTable lv;
 };
@@ -93,7 +101,8 @@ LaunchShape choose_shape(int D, DType dt, uintptr_t align_bits, int64_t pairs);
 // Tile table and workspace layout of a launch covering `nimg` images.
 struct WorkspaceLayout {
   int64_t T, Wmax, Emax;
-  size_t off_count, off_cursor, off_start, off_witem, off_nwork, off_split, off_entries, bytes;
+  size_t off_count, off_cursor, off_start, off_witem, off_nwork, off_split, off_entries, off_stats,
+      off_refpart, bytes;
 };
 WorkspaceLayout workspace_layout(const int64_t *spatial_shapes, int64_t L, int64_t nimg, int64_t M,
                                  int64_t Lq, int64_t K);

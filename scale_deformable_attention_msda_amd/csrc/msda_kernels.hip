@@ -133,19 +133,23 @@ __device__ __forceinline__ float dpp_mov(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
-// Sum over the `lpp` consecutive lanes of a pair; every lane gets the total.
-// Steps: quad xor 1, quad xor 2, mirror within 8, mirror within 16, then
-// cross-row exchanges. Each step adds two disjoint partial sums, so the
-// result is identical in every lane of the group.
-template <int LPP>
+// NaN-propagating maximum (a NaN operand gives NaN whichever side it is on).
+__device__ __forceinline__ float max_nan(float a, float b) { return (b > a || b != b) ? b : a; }
+
+// Sum (or maximum) over the `lpp` consecutive lanes of a pair; every lane
+// gets the result. Steps: quad xor 1, quad xor 2, mirror within 8, mirror
+// within 16, then cross-row exchanges. Each step combines two disjoint
+// partial results, so the sum is identical in every lane of the group.
+template <int LPP, bool MAX = false>
 __device__ __forceinline__ float group_sum(float v, int lpp_rt) {
   const int lpp = LPP > 0 ? LPP : lpp_rt;
-  if (lpp >= 2) v += dpp_mov<0xB1>(v);   // quad_perm [1,0,3,2]
-  if (lpp >= 4) v += dpp_mov<0x4E>(v);   // quad_perm [2,3,0,1]
-  if (lpp >= 8) v += dpp_mov<0x141>(v);  // row_half_mirror
-  if (lpp >= 16) v += dpp_mov<0x140>(v); // row_mirror
-  if (lpp >= 32) v += __shfl_xor(v, 16);
-  if (lpp >= 64) v += __shfl_xor(v, 32);
+  auto op = [](float a, float b) { return MAX ? max_nan(a, b) : a + b; };
+  if (lpp >= 2) v = op(v, dpp_mov<0xB1>(v));   // quad_perm [1,0,3,2]
+  if (lpp >= 4) v = op(v, dpp_mov<0x4E>(v));   // quad_perm [2,3,0,1]
+  if (lpp >= 8) v = op(v, dpp_mov<0x141>(v));  // row_half_mirror
+  if (lpp >= 16) v = op(v, dpp_mov<0x140>(v)); // row_mirror
+  if (lpp >= 32) v = op(v, __shfl_xor(v, 16));
+  if (lpp >= 64) v = op(v, __shfl_xor(v, 32));
   return v;
 }
 
@@ -185,11 +189,10 @@ __device__ __forceinline__ uint32_t pair_base(const Params &p, uint32_t P) {
 __device__ __forceinline__ uint32_t small_div(uint32_t i, uint32_t mg) { return (i * mg) >> 20; }
 __device__ __forceinline__ uint32_t small_magic(uint32_t d) { return ((1u << 20) + d - 1) / d; }
 
-__device__ __forceinline__ Sample sample_geometry(const Params &p, uint32_t base_pair, int64_t gi, int l,
+// Geometry of a sample at normalised location xy with weight A.
+__device__ __forceinline__ Sample sample_geometry(const Params &p, uint32_t base_pair, float2 xy, float A, int l,
                                                   const int32_t *sH, const int32_t *sW,
                                                   const int32_t *sS) {
-  const float2 xy = *reinterpret_cast<const float2 *>(p.loc + 2 * gi);
-  const float A = p.attn[gi];
   const int H = sH[l], W = sW[l], s0 = sS[l];
   float x = fmaf(xy.x, (float)W, -0.5f);
   float y = fmaf(xy.y, (float)H, -0.5f);
@@ -215,6 +218,56 @@ __device__ __forceinline__ Sample sample_geometry(const Params &p, uint32_t base
   return s;
 }
 
+// ------------------------------------------------- fused inputs (optional)
+//
+// The step in front of the sampling core, done in the kernels when the caller
+// passes raw predictions (page "Deformable DETR", section "Deformable
+// attention module": offsets and attention logits come from one linear
+// projection of the query and the logits go through a softmax; section
+// "Multi-scale deformable attention": the softmax runs jointly over a head's
+// L*K samples and the location is the reference point plus an offset in
+// level-l pixels; section "Variants": with boxes as references the offsets
+// are scaled by the box's width and height). Locations are formed in binary32
+// as ref + offset / size (points; quotient and sum each rounded once) or as
+// one fmaf(offset, box size, box centre) (boxes).
+
+__device__ __forceinline__ float softmax_weight(float z, float2 st) { return expf(z - st.x) * st.y; }
+
+// Reference point (x, y, 0, 0) or box (cx, cy, w, h) of the query of pair P.
+__device__ __forceinline__ float4 load_ref(const Params &p, uint32_t P) {
+  const float2 *r = reinterpret_cast<const float2 *>(p.ref + (size_t)(P / (uint32_t)p.M) * (size_t)p.ref_dim);
+  const float2 c = r[0];
+  if (p.ref_dim == 2) return make_float4(c.x, c.y, 0.0f, 0.0f);
+  const float2 wh = r[1];
+  return make_float4(c.x, c.y, wh.x, wh.y);
+}
+
+// Normalised location from the per-sample input v: v itself, or v taken as
+// an offset from the reference `rf` (fused inputs).
+template <bool FUSE>
+__device__ __forceinline__ float2 form_loc(const Params &p, float2 v, int l, float4 rf, const int32_t *sH,
+                                           const int32_t *sW) {
+  if constexpr (!FUSE) return v;
+  if (p.ref_dim == 2) return make_float2(rf.x + v.x / (float)sW[l], rf.y + v.y / (float)sH[l]);
+  return make_float2(fmaf(v.x, rf.z, rf.x), fmaf(v.y, rf.w, rf.y));
+}
+
+// Softmax statistics (max, 1/sum) of a pair's logits z[0, LK), computed by the
+// pair's lpp lanes (lane j takes every lpp-th logit); every lane of the pair
+// gets them. Lanes of inactive pairs only join the exchanges.
+template <int LPP>
+__device__ __forceinline__ float2 pair_softmax_stats(const float *z, bool active, int j, int lpp, int LK) {
+  float mx = -INFINITY;
+  if (active)
+    for (int i = j; i < LK; i += lpp) mx = max_nan(mx, z[i]);
+  mx = group_sum<LPP, true>(mx, lpp);
+  float s = 0.0f;
+  if (active)
+    for (int i = j; i < LK; i += lpp) s += expf(z[i] - mx);
+  s = group_sum<LPP>(s, lpp);
+  return make_float2(mx, 1.0f / s);
+}
+
 // ---------------------------------------------------------------- forward
 
 struct __align__(16) FDesc {
@@ -222,10 +275,12 @@ struct __align__(16) FDesc {
   float w[4];       // attn * bilinear weight, 0 for corners outside the map
 };
 
-template <typename T, int VEC, int NCG, int LPP>
+template <typename T, int VEC, int NCG, int LPP, bool FUSE>
 __global__ __launch_bounds__(kBlock) void fwd_kernel(const Params p) {
   __shared__ FDesc desc[kDescCap];
   __shared__ uint32_t pbase[kBlock];
+  __shared__ float4 sref[FUSE ? kBlock : 1];  // reference of each pair's query
+  __shared__ float2 sst[FUSE ? kBlock : 1];   // softmax statistics of each pair
   __shared__ int32_t sH[kMaxLevels], sW[kMaxLevels], sS[kMaxLevels];
   load_levels(p, sH, sW, sS);
 
@@ -241,6 +296,11 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(const Params p) {
   const int j = tid - g * lpp;
   const bool active = g < npairs;
   if (tid < npairs) pbase[tid] = pair_base(p, (uint32_t)(P0 + tid));
+  if constexpr (FUSE) {
+    if (tid < npairs) sref[tid] = load_ref(p, (uint32_t)(P0 + tid));
+    const float2 st = pair_softmax_stats<LPP>(p.attn + (active ? (P0 + g) * p.LK : 0), active, j, lpp, p.LK);
+    if (active && j == 0) sst[g] = st;
+  }
   const uint32_t kmg = small_magic((uint32_t)p.K);
 
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.value, p.value_elems * (uint32_t)T::size);
@@ -266,8 +326,17 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(const Params p) {
       const int gg = (int)small_div((uint32_t)i, pmg);
       const int pp = i - gg * pcn;
       const int pt = pc0 + pp;
-      const Sample s = sample_geometry(p, pbase[gg], (P0 + gg) * p.LK + pt, (int)small_div((uint32_t)pt, kmg),
-                                       sH, sW, sS);
+      const int l = (int)small_div((uint32_t)pt, kmg);
+      const int64_t gi = (P0 + gg) * p.LK + pt;
+      const float2 v = *reinterpret_cast<const float2 *>(p.loc + 2 * gi);
+      const float z = p.attn[gi];
+      float2 xy = v;
+      float A = z;
+      if constexpr (FUSE) {
+        xy = form_loc<true>(p, v, l, sref[gg], sH, sW);
+        A = softmax_weight(z, sst[gg]);
+      }
+      const Sample s = sample_geometry(p, pbase[gg], xy, A, l, sH, sW, sS);
       FDesc d;
       const float wa[2] = {1.0f - s.a, s.a};
       const float wb[2] = {1.0f - s.b, s.b};
@@ -331,18 +400,32 @@ struct __align__(16) BDesc {
   float aw, ah;     // attn * W_l, attn * H_l (chain rule through loc * W - 0.5)
 };
 
-constexpr size_t kSampleSmem =
+constexpr size_t kSampleSmemPlain =
     kDescCap * sizeof(BDesc) + kDescCap * sizeof(float3) + 3 * kMaxLevels * 4 + kBlock * 4;
+// fused inputs add per pair: reference, softmax statistics, sum of A * grad_attn;
+// per staged sample: its weight and its offset
+constexpr size_t kSampleSmemFused = kSampleSmemPlain + kBlock * (16 + 8 + 4) + kDescCap * (4 + 8);
+template <bool FUSE>
+constexpr size_t sample_smem() { return FUSE ? kSampleSmemFused : kSampleSmemPlain; }
 
 // grad_attn and grad_loc of the pairs of logical block `block` (of `nblocks`),
-// with LDS carved from `smem` (kSampleSmem bytes).
-template <typename T, int VEC, int NCG, int LPP>
+// with LDS carved from `smem` (sample_smem<FUSE>() bytes). With fused inputs
+// they become the logit and offset gradients: through the softmax,
+// d/dz_i = A_i (grad_attn_i - sum_j A_j grad_attn_j); through the location,
+// d/d offset = grad_loc / size (points) or grad_loc * box size (boxes); and the
+// pair's sums for the reference gradient go to the workspace.
+template <typename T, int VEC, int NCG, int LPP, bool FUSE>
 __device__ __forceinline__ void bwd_sample_body(const Params &p, int block, int nblocks, unsigned char *smem) {
   BDesc *desc = reinterpret_cast<BDesc *>(smem);
   float3 *res = reinterpret_cast<float3 *>(smem + kDescCap * sizeof(BDesc));
   int32_t *sH = reinterpret_cast<int32_t *>(smem + kDescCap * (sizeof(BDesc) + sizeof(float3)));
   int32_t *sW = sH + kMaxLevels, *sS = sW + kMaxLevels;
   uint32_t *pbase = reinterpret_cast<uint32_t *>(sS + kMaxLevels);
+  float4 *sref = reinterpret_cast<float4 *>(smem + kSampleSmemPlain);  // used with FUSE only
+  float2 *sst = reinterpret_cast<float2 *>(sref + kBlock);
+  float *ssum = reinterpret_cast<float *>(sst + kBlock);
+  float *sA = ssum + kBlock;
+  float2 *soff = reinterpret_cast<float2 *>(sA + kDescCap);
   load_levels(p, sH, sW, sS);
 
   const int tid = threadIdx.x;
@@ -355,6 +438,14 @@ __device__ __forceinline__ void bwd_sample_body(const Params &p, int block, int 
   const int j = tid - g * lpp;
   const bool active = g < npairs;
   if (tid < npairs) pbase[tid] = pair_base(p, (uint32_t)(P0 + tid));
+  if constexpr (FUSE) {
+    if (tid < npairs) {
+      sref[tid] = load_ref(p, (uint32_t)(P0 + tid));
+      sst[tid] = *reinterpret_cast<const float2 *>(p.ws.stats + 2 * (P0 + tid));
+    }
+  }
+  // the pair's sums over its samples (identical in all its lanes)
+  float acc_s = 0.0f, acc_rx = 0.0f, acc_ry = 0.0f, acc_bx = 0.0f, acc_by = 0.0f;
   const uint32_t kmg = small_magic((uint32_t)p.K);
 
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.value, p.value_elems * (uint32_t)T::size);
@@ -379,7 +470,19 @@ __device__ __forceinline__ void bwd_sample_body(const Params &p, int block, int 
       const int pp = i - gg * pcn;
       const int pt = pc0 + pp;
       const int l = (int)small_div((uint32_t)pt, kmg);
-      const Sample s = sample_geometry(p, pbase[gg], (P0 + gg) * p.LK + pt, l, sH, sW, sS);
+      const int64_t gi = (P0 + gg) * p.LK + pt;
+      const float2 v = *reinterpret_cast<const float2 *>(p.loc + 2 * gi);
+      const float z = p.attn[gi];
+      float2 xy = v;
+      float A = z;
+      if constexpr (FUSE) {
+        xy = form_loc<true>(p, v, l, sref[gg], sH, sW);
+        A = softmax_weight(z, sst[gg]);
+        // the softmax gradient needs every sample's weight, in the map or not
+        sA[pp * dstride + gg] = A;
+        soff[pp * dstride + gg] = v;
+      }
+      const Sample s = sample_geometry(p, pbase[gg], xy, A, l, sH, sW, sS);
       BDesc d;
 #pragma unroll
       for (int c = 0; c < 4; ++c) d.off[c] = s.off[c];
@@ -412,7 +515,16 @@ __device__ __forceinline__ void bwd_sample_body(const Params &p, int block, int 
         ga = group_sum<LPP>(ga, lpp);
         gx = group_sum<LPP>(gx, lpp);
         gy = group_sum<LPP>(gy, lpp);
-        if (j == 0) res[pp * dstride + g] = make_float3(ga, d.aw * gx, d.ah * gy);
+        const float glx = d.aw * gx, gly = d.ah * gy;
+        if (j == 0) res[pp * dstride + g] = make_float3(ga, glx, gly);
+        if constexpr (FUSE) {
+          acc_s = fmaf(sA[pp * dstride + g], ga, acc_s);
+          acc_rx += glx;
+          acc_ry += gly;
+          const float2 o = soff[pp * dstride + g];
+          acc_bx = fmaf(glx, o.x, acc_bx);
+          acc_by = fmaf(gly, o.y, acc_by);
+        }
       }
     }
     __syncthreads();
@@ -421,16 +533,42 @@ __device__ __forceinline__ void bwd_sample_body(const Params &p, int block, int 
       const int pp = i - gg * pcn;
       const float3 r = res[pp * dstride + gg];
       const int64_t gi = (P0 + gg) * p.LK + pc0 + pp;
-      p.grad_attn[gi] = r.x;
-      *reinterpret_cast<float2 *>(p.grad_loc + 2 * gi) = make_float2(r.y, r.z);
+      p.grad_attn[gi] = r.x;  // fused inputs: finished below, once the pair's sum is known
+      float2 gl = make_float2(r.y, r.z);
+      if constexpr (FUSE) {
+        if (p.ref_dim == 2) {
+          const int l = (pc0 + pp) / p.K;
+          gl = make_float2(r.y / (float)sW[l], r.z / (float)sH[l]);
+        } else {
+          const float4 rf = sref[gg];
+          gl = make_float2(r.y * rf.z, r.z * rf.w);
+        }
+      }
+      *reinterpret_cast<float2 *>(p.grad_loc + 2 * gi) = gl;
+    }
+  }
+  if constexpr (FUSE) {
+    if (active && j == 0) {
+      ssum[g] = acc_s;
+      if (p.grad_ref)
+        *reinterpret_cast<float4 *>(p.ws.ref_part + 4 * (P0 + g)) = make_float4(acc_rx, acc_ry, acc_bx, acc_by);
+    }
+    __syncthreads();
+    // grad_logits from this block's grad_attn values (written above by the
+    // block itself and visible after the barrier)
+    for (int i = tid; i < npairs * p.LK; i += kBlock) {
+      const int gg = i / p.LK;
+      const int64_t gi = P0 * p.LK + i;
+      const float A = softmax_weight(p.attn[gi], sst[gg]);
+      p.grad_attn[gi] = A * (p.grad_attn[gi] - ssum[gg]);
     }
   }
 }
 
-template <typename T, int VEC, int NCG, int LPP>
+template <typename T, int VEC, int NCG, int LPP, bool FUSE>
 __global__ __launch_bounds__(kBlock) void bwd_sample_kernel(const Params p) {
-  __shared__ __align__(16) unsigned char smem[kSampleSmem];
-  bwd_sample_body<T, VEC, NCG, LPP>(p, blockIdx.x, gridDim.x, smem);
+  __shared__ __align__(16) unsigned char smem[sample_smem<FUSE>()];
+  bwd_sample_body<T, VEC, NCG, LPP, FUSE>(p, blockIdx.x, gridDim.x, smem);
 }
 
 // ------------------------------------------------------ tile binning (sort)
@@ -487,7 +625,7 @@ __device__ __forceinline__ void zero_split_body(const Params &p, int block, int 
                                                 const int32_t *sW, const int32_t *sS, const int32_t *sTW,
                                                 const int32_t *sToff);
 
-template <int MODE>
+template <int MODE, bool FUSE>
 __global__ __launch_bounds__(kBlock) void bin_kernel(const Params p) {
   __shared__ uint32_t cnt[kBinCap];
   __shared__ uint32_t gbase[MODE == 1 ? kBinCap : 1];
@@ -512,6 +650,18 @@ __global__ __launch_bounds__(kBlock) void bin_kernel(const Params p) {
   uint4 *rec_out = reinterpret_cast<uint4 *>(p.ws.entries);
   if (local)
     for (int i = tid; i < p.TPI; i += kBlock) cnt[i] = 0;
+  if constexpr (FUSE && MODE == 0) {
+    // softmax statistics of the workgroup's pairs, read by the later passes
+    for (int qi = tid; qi < nsamp / p.LK; qi += kBlock) {
+      const int64_t P = ((int64_t)n * p.Lq + q0 + qi) * p.M + m;
+      const float *z = p.attn + P * p.LK;
+      float mx = -INFINITY;
+      for (int i = 0; i < p.LK; ++i) mx = max_nan(mx, z[i]);
+      float sum = 0.0f;
+      for (int i = 0; i < p.LK; ++i) sum += expf(z[i] - mx);
+      *reinterpret_cast<float2 *>(p.ws.stats + 2 * P) = make_float2(mx, 1.0f / sum);
+    }
+  }
   __syncthreads();
 
   // Up to four tiles per sample, in fixed slots (dy, dx) so that every array
@@ -529,11 +679,16 @@ __global__ __launch_bounds__(kBlock) void bin_kernel(const Params p) {
     const int pt = i - qi * p.LK;
     const uint32_t P = (uint32_t)(((int64_t)n * p.Lq + q0 + qi) * p.M + m);
     const int64_t sid = (int64_t)P * p.LK + pt;
-    const float2 xy = *reinterpret_cast<const float2 *>(p.loc + 2 * sid);
     const int l = pt / p.K;
+    float2 xy = *reinterpret_cast<const float2 *>(p.loc + 2 * sid);
+    if constexpr (FUSE) xy = form_loc<true>(p, xy, l, load_ref(p, P), sH, sW);
     Footprint f;
     if (!sample_footprint(xy.x, xy.y, sH[l], sW[l], f)) continue;
-    if (MODE == 1) rec[r] = make_uint4(P, __float_as_uint(f.x), __float_as_uint(f.y), __float_as_uint(p.attn[sid]));
+    if (MODE == 1) {
+      float A = p.attn[sid];
+      if constexpr (FUSE) A = softmax_weight(A, *reinterpret_cast<const float2 *>(p.ws.stats + 2 * (int64_t)P));
+      rec[r] = make_uint4(P, __float_as_uint(f.x), __float_as_uint(f.y), __float_as_uint(A));
+    }
     // tile rows/columns touched by the in-map corners
     const int ya = f.r0 ? f.y0 : f.y0 + 1, yb = f.r1 ? f.y0 + 1 : f.y0;
     const int xa = f.c0 ? f.x0 : f.x0 + 1, xb = f.c1 ? f.x0 + 1 : f.x0;
@@ -844,14 +999,29 @@ __global__ __launch_bounds__(kBlock) void gv_kernel(const Params p) {
 // two are independent, so the sample gradients fill the machine while the
 // crowded tiles' items finish. Blocks [0, gv_blocks) are grad_value items
 // (one channel group when D <= 64), the rest run bwd_sample_body.
-template <typename T, int VEC, int NCG, int LPP, int CS>
+template <typename T, int VEC, int NCG, int LPP, int CS, bool FUSE>
 __global__ __launch_bounds__(kBlock) void bwd_fused_kernel(const Params p) {
-  constexpr size_t kSmem = kGvSmem > kSampleSmem ? kGvSmem : kSampleSmem;
+  constexpr size_t kSmem = kGvSmem > sample_smem<FUSE>() ? kGvSmem : sample_smem<FUSE>();
   __shared__ __align__(16) unsigned char smem[kSmem];
   if ((int)blockIdx.x < p.gv_blocks)
     gv_body<T, CS>(p, blockIdx.x, 0, smem);
   else
-    bwd_sample_body<T, VEC, NCG, LPP>(p, (int)blockIdx.x - p.gv_blocks, (int)gridDim.x - p.gv_blocks, smem);
+    bwd_sample_body<T, VEC, NCG, LPP, FUSE>(p, (int)blockIdx.x - p.gv_blocks, (int)gridDim.x - p.gv_blocks,
+                                            smem);
+}
+
+// Reference gradient of each query (fused inputs): the sum over its M pairs of
+// the per-pair sums that the sample pass left in the workspace, in a fixed
+// order. Thread i owns component i % ref_dim of query i / ref_dim.
+__global__ __launch_bounds__(kBlock) void ref_grad_kernel(const Params p) {
+  const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  const int64_t nq = p.pairs / p.M;
+  if (i >= nq * p.ref_dim) return;
+  const int64_t q = i / p.ref_dim;
+  const int c = (int)(i - q * p.ref_dim);
+  float sum = 0.0f;
+  for (int m = 0; m < p.M; ++m) sum += p.ws.ref_part[(q * p.M + m) * 4 + c];
+  p.grad_ref[i] = sum;
 }
 
 __global__ __launch_bounds__(kBlock) void zero_u32_kernel(uint32_t *ptr, int64_t n) {
@@ -879,43 +1049,48 @@ __global__ __launch_bounds__(kBlock) void zero_kernel_unaligned(float *ptr, int6
 
 using KernelFn = void (*)(Params);
 
-template <typename T, int VEC>
+template <typename T, int VEC, bool FUSE>
 KernelFn pick(bool fwd, int ncg, int lpp) {
   // Compile-time lane counts for the common 16-byte shapes (fp32 D=32 and
   // bf16 D=32), a runtime lane count otherwise.
   if (ncg == 1 && lpp == 8 && VEC * T::size == 16)
-    return fwd ? fwd_kernel<T, VEC, 1, 8> : bwd_sample_kernel<T, VEC, 1, 8>;
+    return fwd ? fwd_kernel<T, VEC, 1, 8, FUSE> : bwd_sample_kernel<T, VEC, 1, 8, FUSE>;
   if (ncg == 1 && lpp == 4 && VEC * T::size == 16)
-    return fwd ? fwd_kernel<T, VEC, 1, 4> : bwd_sample_kernel<T, VEC, 1, 4>;
+    return fwd ? fwd_kernel<T, VEC, 1, 4, FUSE> : bwd_sample_kernel<T, VEC, 1, 4, FUSE>;
   switch (ncg) {
-    case 1: return fwd ? fwd_kernel<T, VEC, 1, 0> : bwd_sample_kernel<T, VEC, 1, 0>;
-    case 2: return fwd ? fwd_kernel<T, VEC, 2, 0> : bwd_sample_kernel<T, VEC, 2, 0>;
-    case 4: return fwd ? fwd_kernel<T, VEC, 4, 0> : bwd_sample_kernel<T, VEC, 4, 0>;
+    case 1: return fwd ? fwd_kernel<T, VEC, 1, 0, FUSE> : bwd_sample_kernel<T, VEC, 1, 0, FUSE>;
+    case 2: return fwd ? fwd_kernel<T, VEC, 2, 0, FUSE> : bwd_sample_kernel<T, VEC, 2, 0, FUSE>;
+    case 4: return fwd ? fwd_kernel<T, VEC, 4, 0, FUSE> : bwd_sample_kernel<T, VEC, 4, 0, FUSE>;
     default: break;
   }
   if constexpr (VEC == 1) {
-    if (ncg == 8) return fwd ? fwd_kernel<T, 1, 8, 0> : bwd_sample_kernel<T, 1, 8, 0>;
-    if (ncg == 16) return fwd ? fwd_kernel<T, 1, 16, 0> : bwd_sample_kernel<T, 1, 16, 0>;
+    if (ncg == 8) return fwd ? fwd_kernel<T, 1, 8, 0, FUSE> : bwd_sample_kernel<T, 1, 8, 0, FUSE>;
+    if (ncg == 16) return fwd ? fwd_kernel<T, 1, 16, 0, FUSE> : bwd_sample_kernel<T, 1, 16, 0, FUSE>;
   }
   return nullptr;
 }
 
-KernelFn select(bool fwd, DType dt, const LaunchShape &s) {
+template <bool FUSE>
+KernelFn select_t(bool fwd, DType dt, const LaunchShape &s) {
   if (dt == DType::F32) {
     switch (s.vec) {
-      case 4: return pick<F32, 4>(fwd, s.ncg, s.lpp);
-      case 2: return pick<F32, 2>(fwd, s.ncg, s.lpp);
-      case 1: return pick<F32, 1>(fwd, s.ncg, s.lpp);
+      case 4: return pick<F32, 4, FUSE>(fwd, s.ncg, s.lpp);
+      case 2: return pick<F32, 2, FUSE>(fwd, s.ncg, s.lpp);
+      case 1: return pick<F32, 1, FUSE>(fwd, s.ncg, s.lpp);
     }
   } else {
     switch (s.vec) {
-      case 8: return pick<BF16, 8>(fwd, s.ncg, s.lpp);
-      case 4: return pick<BF16, 4>(fwd, s.ncg, s.lpp);
-      case 2: return pick<BF16, 2>(fwd, s.ncg, s.lpp);
-      case 1: return pick<BF16, 1>(fwd, s.ncg, s.lpp);
+      case 8: return pick<BF16, 8, FUSE>(fwd, s.ncg, s.lpp);
+      case 4: return pick<BF16, 4, FUSE>(fwd, s.ncg, s.lpp);
+      case 2: return pick<BF16, 2, FUSE>(fwd, s.ncg, s.lpp);
+      case 1: return pick<BF16, 1, FUSE>(fwd, s.ncg, s.lpp);
     }
   }
   return nullptr;
+}
+
+KernelFn select(bool fwd, bool fuse, DType dt, const LaunchShape &s) {
+  return fuse ? select_t<true>(fwd, dt, s) : select_t<false>(fwd, dt, s);
 }
 
 template <typename T>
@@ -937,7 +1112,7 @@ hipError_t launch_fn(const void *fn, int64_t blocks, int threads, int gy, Params
 }
 
 hipError_t launch_pairs(bool fwd, const Params &p_in, DType dt, const LaunchShape &s, hipStream_t stream) {
-  KernelFn fn = select(fwd, dt, s);
+  KernelFn fn = select(fwd, p_in.ref_dim != 0, dt, s);
   if (!fn) return hipErrorInvalidValue;
   Params p = p_in;
   p.lpp = s.lpp;
@@ -1016,6 +1191,9 @@ WorkspaceLayout workspace_layout(const int64_t *spatial_shapes, int64_t L, int64
   w.off_nwork = o;   o = up(o + 4);
   w.off_split = o;   o = up(o + 4 * (size_t)w.T);
   w.off_entries = o; o = up(o + 16 * (size_t)w.Emax);
+  // fused inputs: softmax statistics and reference-gradient sums per pair
+  w.off_stats = o;   o = up(o + 8 * (size_t)(nimg * Lq * M));
+  w.off_refpart = o; o = up(o + 16 * (size_t)(nimg * Lq * M));
   w.bytes = o;
   return w;
 }
@@ -1049,13 +1227,15 @@ hipError_t launch_backward(const Params &p_in, DType dt, const LaunchShape &s, h
   }
   // 2. counting sort of (sample, tile) entries; the scatter launch also clears
   //    the tiles whose grad_value is summed over several work items
+  const bool fuse = p.ref_dim != 0;
   const int64_t bin_blocks = (int64_t)p.N * p.M * ((p.Lq + p.qpb - 1) / p.qpb);
-  if ((e = launch_fn(reinterpret_cast<const void *>(bin_kernel<0>), bin_blocks, kBlock, 1, p, stream)) != hipSuccess)
-    return e;
+  const void *bin0 = fuse ? reinterpret_cast<const void *>(bin_kernel<0, true>)
+                          : reinterpret_cast<const void *>(bin_kernel<0, false>);
+  const void *bin1 = fuse ? reinterpret_cast<const void *>(bin_kernel<1, true>)
+                          : reinterpret_cast<const void *>(bin_kernel<1, false>);
+  if ((e = launch_fn(bin0, bin_blocks, kBlock, 1, p, stream)) != hipSuccess) return e;
   if ((e = launch_fn(reinterpret_cast<const void *>(scan_kernel), 1, 1024, 1, p, stream)) != hipSuccess) return e;
-  if ((e = launch_fn(reinterpret_cast<const void *>(bin_kernel<1>), bin_blocks + 256, kBlock, 1, p, stream)) !=
-      hipSuccess)
-    return e;
+  if ((e = launch_fn(bin1, bin_blocks + 256, kBlock, 1, p, stream)) != hipSuccess) return e;
   // 3. grad_value per tile, and grad_attn / grad_loc per sample
   const int64_t wmax = p.T + (4 * p.pairs * p.LK + kPartEntries - 1) / kPartEntries;
   const int Dc = min(kChanGroup, p.D);
@@ -1073,13 +1253,26 @@ hipError_t launch_backward(const Params &p_in, DType dt, const LaunchShape &s, h
   const int64_t gvb = (wmax + 7) & ~(int64_t)7;
   if ((hot_f32 || hot_bf16) && groups == 1 && gvb + sample_blocks <= 0x7fffffff) {
     p.gv_blocks = (int32_t)gvb;
-    const void *fn = hot_f32 ? reinterpret_cast<const void *>(bwd_fused_kernel<F32, 4, 1, 8, 8>)
-                             : reinterpret_cast<const void *>(bwd_fused_kernel<BF16, 8, 1, 4, 8>);
-    return launch_fn(fn, gvb + sample_blocks, kBlock, 1, p, stream);
+    const void *fn;
+    if (hot_f32)
+      fn = fuse ? reinterpret_cast<const void *>(bwd_fused_kernel<F32, 4, 1, 8, 8, true>)
+                : reinterpret_cast<const void *>(bwd_fused_kernel<F32, 4, 1, 8, 8, false>);
+    else
+      fn = fuse ? reinterpret_cast<const void *>(bwd_fused_kernel<BF16, 8, 1, 4, 8, true>)
+                : reinterpret_cast<const void *>(bwd_fused_kernel<BF16, 8, 1, 4, 8, false>);
+    if ((e = launch_fn(fn, gvb + sample_blocks, kBlock, 1, p, stream)) != hipSuccess) return e;
+  } else {
+    if ((e = launch_pairs(false, p, dt, s, stream)) != hipSuccess) return e;
+    KernelFn gv = dt == DType::F32 ? pick_gv<F32>(cs) : pick_gv<BF16>(cs);
+    if ((e = launch_fn(reinterpret_cast<const void *>(gv), wmax, kBlock, groups, p, stream)) != hipSuccess)
+      return e;
   }
-  if ((e = launch_pairs(false, p, dt, s, stream)) != hipSuccess) return e;
-  KernelFn gv = dt == DType::F32 ? pick_gv<F32>(cs) : pick_gv<BF16>(cs);
-  return launch_fn(reinterpret_cast<const void *>(gv), wmax, kBlock, groups, p, stream);
+  // 4. reference gradients (fused inputs, when asked for)
+  if (fuse && p.grad_ref) {
+    const int64_t n = p.pairs / p.M * p.ref_dim;
+    return launch_fn(reinterpret_cast<const void *>(ref_grad_kernel), (n + kBlock - 1) / kBlock, kBlock, 1, p, stream);
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_zero(float *ptr, int64_t n, hipStream_t stream) {

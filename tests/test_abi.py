@@ -28,7 +28,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["msda_backward", "msda_backward_workspace_size", "msda_forward",
-                                    "msda_status_string", "msda_validate"]
+                                    "msda_fused_backward", "msda_fused_forward", "msda_status_string",
+                                    "msda_validate"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -122,11 +123,40 @@ def test_entry_points_reject_bad_pointers_before_any_hip_call():
     assert lib.msda_forward(None, ss, ls, None, None, None, 1, 22223, 8, 32, 4, 0, 4, 0, None) == 0
 
 
+def test_fused_entry_points_reject_bad_arguments_before_any_hip_call():
+    lib = binding.load_library()
+    ss = COCO.ctypes.data
+    ls = STARTS.ctypes.data
+    dims = (1, 22223, 8, 32, 4, 22223, 4)
+    A, W, WB = 0x10000, 0x100000, 1 << 40
+    # reference layout: 2 (points) or 4 (boxes) floats per query
+    for rd in (0, 1, 3, 5, -2):
+        assert lib.msda_fused_forward(A, ss, ls, A, rd, A, A, A, *dims, 0, None) == 1
+        assert lib.msda_fused_backward(A, ss, ls, A, rd, A, A, A, A, A, A, A, *dims, 0, W, WB, None) == 1
+    # null reference, null outputs; grad_ref alone may be null (not computed)
+    assert lib.msda_fused_forward(A, ss, ls, None, 2, A, A, A, *dims, 0, None) == 1
+    assert lib.msda_fused_forward(A, ss, ls, A, 4, A, A, None, *dims, 0, None) == 1
+    assert lib.msda_fused_backward(A, ss, ls, None, 4, A, A, A, A, A, A, A, *dims, 0, W, WB, None) == 1
+    assert lib.msda_fused_backward(A, ss, ls, A, 2, A, A, A, A, None, A, None, *dims, 0, W, WB, None) == 1
+    # alignment: ref and offsets 8 bytes, logits and grad_ref 4 bytes
+    assert lib.msda_fused_forward(A, ss, ls, A + 4, 2, A, A, A, *dims, 0, None) == 3
+    assert lib.msda_fused_forward(A, ss, ls, A, 2, A + 4, A, A, *dims, 0, None) == 3
+    assert lib.msda_fused_forward(A, ss, ls, A, 2, A, A + 2, A, *dims, 0, None) == 3
+    assert lib.msda_fused_backward(A, ss, ls, A, 4, A, A, A, A, A, A, A + 2, *dims, 0, W, WB, None) == 3
+    assert lib.msda_fused_backward(A, ss, ls, A, 4, A, A, A, A, A + 4, A, A, *dims, 0, W, WB, None) == 3
+    # workspace as for the sampling core's backward
+    assert lib.msda_fused_backward(A, ss, ls, A, 4, A, A, A, A, A, A, A, *dims, 0, W, 1024, None) == 5
+    # empty problems are no-ops
+    assert lib.msda_fused_forward(None, ss, ls, None, 2, None, None, None, 0, 22223, 8, 32, 4, 10, 4, 0,
+                                  None) == 0
+
+
 def test_workspace_size_and_overlapping_levels():
     lib = binding.load_library()
     n = msda.msda_backward_workspace_size(COCO, STARTS, 2, 22223, 8, 32, 4, 22223, 4)
     samples = 2 * 22223 * 8 * 4 * 4
-    assert 64 * samples <= n <= 64 * samples + (1 << 20)
+    pairs = 2 * 22223 * 8
+    assert 64 * samples + 24 * pairs <= n <= 64 * samples + 24 * pairs + (1 << 20)
     # overlapping level row ranges are rejected
     ss = np.array([[4, 4], [2, 2]], dtype=np.int64)
     ls = np.array([0, 14], dtype=np.int64)

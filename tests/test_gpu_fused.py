@@ -1,0 +1,234 @@
+"""Parity of the fused entry points (softmax of logits and location formation
+inside the kernels) with the fp64 oracle, through the C ABI.
+
+Tolerances follow the sampling core's: out, grad_value and grad_logits
+max-abs <= 1e-5 (float32 arithmetic; bf16 out within one bf16 ulp); offset
+gradients in pixel units of their level (points: they already are; boxes:
+divided by (w * W_l, h * H_l)) max-abs <= 1e-5. grad_ref sums grad_loc over the
+M*L*K samples of a query, so its bound is the sum of those samples' bounds:
+1e-5 * sum W_l (x) or H_l (y) for the centre, and that sum weighted by |offset|
+for the box size.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import msda_fused_backward, msda_fused_forward, msda_grad_value_rows  # noqa: E402
+from oracle import fused_locations, softmax_weights  # noqa: E402
+from tests.gpu_util import (assert_f32, assert_normwise, bf16_ulp, max_abs, note, to_f64)  # noqa: E402
+import scale_deformable_attention_msda_amd as msda  # noqa: E402
+from workloads import COCO_LEVELS, fused_workload  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+SMALL_LEVELS = ((20, 34), (10, 17), (5, 9), (3, 5))
+
+
+def _dev(w, device="cuda:0"):
+    if w.dtype == "bf16":
+        value = torch.from_numpy(w.value_bits.view(np.int16).copy()).view(torch.bfloat16).to(device)
+    else:
+        value = torch.from_numpy(w.value).to(device)
+    ref = torch.from_numpy(w.ref).to(device)
+    off = torch.from_numpy(w.offsets).to(device)
+    logits = torch.from_numpy(w.logits).to(device)
+    g = None
+    if w.grad_out is not None:
+        if w.dtype == "bf16":
+            g = torch.from_numpy(w.grad_out_bits.view(np.int16).copy()).view(torch.bfloat16).to(device)
+        else:
+            g = torch.from_numpy(w.grad_out).to(device)
+    return value, ref, off, logits, g
+
+
+def _oracle_args(w):
+    return (w.value, w.spatial_shapes, w.level_start, w.ref, w.offsets, w.logits)
+
+
+def _check_out(w, got, ref):
+    if w.dtype == "f32":
+        assert_f32("out", got, ref)
+        return
+    assert_normwise("out", got, ref)
+    bad = np.abs(got - ref) > bf16_ulp(ref) + 1e-5
+    assert not bad.any(), f"{bad.sum()} bf16 outputs beyond one ulp; worst {max_abs(got, ref):.3e}"
+
+
+def _pixel_offsets(w, g_off, ref_rows):
+    """Offset gradients in pixel units of their level: points are already; boxes
+    are divided by (w * W_l, h * H_l). ref_rows: the reference rows [..., ref_dim]
+    matching g_off's leading axes."""
+    g_off = np.asarray(g_off, np.float64)
+    if w.ref.shape[-1] == 2:
+        return g_off
+    ss = w.spatial_shapes
+    size = np.stack([ss[:, 1], ss[:, 0]], axis=-1).reshape(-1, 1, 2).astype(np.float64)  # [L,1,2]
+    box = np.asarray(ref_rows, np.float64)[..., None, None, None, 2:]
+    return g_off / (size * box)
+
+
+def _ref_bound(w, off_rows):
+    """Per-element bound of grad_ref [..., ref_dim] for queries with offsets off_rows [..., M, L, K, 2]."""
+    ss = w.spatial_shapes
+    size = np.stack([ss[:, 1], ss[:, 0]], axis=-1).reshape(-1, 1, 2).astype(np.float64)  # (W_l, H_l)
+    off_rows = np.asarray(off_rows, np.float64)
+    centre = 1e-5 * np.broadcast_to(size, off_rows.shape).sum(axis=(-4, -3, -2))
+    if w.ref.shape[-1] == 2:
+        return centre
+    return np.concatenate([centre, 1e-5 * (size * np.abs(off_rows)).sum(axis=(-4, -3, -2))], axis=-1)
+
+
+def _check_grads(w, got, ref, ref_rows, off_rows, check_gv=True):
+    gv, go, gz, gr = got
+    rgv, rgo, rgz, rgr = ref
+    if check_gv:
+        assert_f32("grad_value", gv, rgv)
+    assert_f32("grad_logits", gz, rgz)
+    assert_f32("grad_offsets (pixel units)", _pixel_offsets(w, go, ref_rows), _pixel_offsets(w, rgo, ref_rows))
+    if gr is not None:
+        assert np.all(np.isfinite(gr)), "grad_ref: non-finite values"
+        excess = np.abs(np.asarray(gr, np.float64) - rgr) - _ref_bound(w, off_rows)
+        assert excess.max() <= 0, f"grad_ref beyond its bound by {excess.max():.3e}"
+
+
+def _gpu_fused_backward(w, **kw):
+    value, ref, off, logits, g = _dev(w)
+    res = msda.msda_fused_backward(value, w.spatial_shapes, w.level_start, ref, off, logits, g, **kw)
+    torch.cuda.synchronize()
+    return tuple(None if t is None else to_f64(t) for t in res)
+
+
+# ------------------------------------------------------------------ forward
+
+@pytest.mark.parametrize("kind,ref_dim,dtype", [("encoder", 2, "f32"), ("encoder", 2, "bf16")])
+def test_fused_forward_encoder_small_maps_full(kind, ref_dim, dtype):
+    w = fused_workload(kind, N=2, shapes=SMALL_LEVELS, ref_dim=ref_dim, dtype=dtype, seed=31)
+    note(f"fused forward {kind} ref_dim={ref_dim} {dtype} small maps")
+    value, ref, off, logits, _ = _dev(w)
+    out = to_f64(msda.msda_fused_forward(value, w.spatial_shapes, w.level_start, ref, off, logits))
+    torch.cuda.synchronize()
+    _check_out(w, out, msda_fused_forward(*_oracle_args(w)))
+
+
+@pytest.mark.parametrize("ref_dim,dtype", [(2, "bf16"), (4, "bf16"), (2, "f32"), (4, "f32")])
+def test_fused_forward_decoder_full_config(ref_dim, dtype):
+    w = fused_workload("decoder", N=2, Lq=300, ref_dim=ref_dim, dtype=dtype, seed=32 + ref_dim)
+    note(f"fused forward decoder N=2 Lq=300 COCO levels ref_dim={ref_dim} {dtype}")
+    value, ref, off, logits, _ = _dev(w)
+    out = to_f64(msda.msda_fused_forward(value, w.spatial_shapes, w.level_start, ref, off, logits))
+    torch.cuda.synchronize()
+    _check_out(w, out, msda_fused_forward(*_oracle_args(w)))
+
+
+# ----------------------------------------------------------------- backward
+
+@pytest.mark.parametrize("K", [4, 8])
+def test_fused_backward_encoder_small_maps_full(K):
+    w = fused_workload("encoder", N=2, shapes=SMALL_LEVELS, K=K, seed=40 + K, with_grad=True)
+    note(f"fused backward encoder points K={K} f32 small maps")
+    got = _gpu_fused_backward(w)
+    ref = msda_fused_backward(*_oracle_args(w), w.grad_out)
+    _check_grads(w, got, ref, w.ref, w.offsets)
+
+
+@pytest.mark.parametrize("ref_dim,dtype", [(2, "f32"), (4, "f32"), (4, "bf16")])
+def test_fused_backward_decoder_full_config(ref_dim, dtype):
+    w = fused_workload("decoder", N=2, Lq=300, ref_dim=ref_dim, dtype=dtype, seed=50 + ref_dim, with_grad=True)
+    note(f"fused backward decoder N=2 Lq=300 ref_dim={ref_dim} {dtype}")
+    got = _gpu_fused_backward(w)
+    ref = msda_fused_backward(*_oracle_args(w), w.grad_out)
+    # bf16 inputs are exact values and the arithmetic is float32: same bar
+    _check_grads(w, got, ref, w.ref, w.offsets)
+
+
+def test_fused_backward_encoder_full_size_sampled():
+    w = fused_workload("encoder", N=2, shapes=COCO_LEVELS, K=4, seed=60, with_grad=True)
+    d = w.dims
+    note("fused backward encoder full size N=2 S=Lq=22223 M=8 D=32 K=4 f32")
+    value, ref, off, logits, g = _dev(w)
+    gv, go, gz, gr = msda.msda_fused_backward(value, w.spatial_shapes, w.level_start, ref, off, logits, g)
+    out = msda.msda_fused_forward(value, w.spatial_shapes, w.level_start, ref, off, logits)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(61)
+    qn = rng.integers(0, d["N"], 800)
+    qq = rng.integers(0, d["Lq"], 800)
+    qn[0], qq[0], qn[1], qq[1] = 0, 0, d["N"] - 1, d["Lq"] - 1
+    _, rgo, rgz, rgr = msda_fused_backward(*_oracle_args(w), w.grad_out, queries=(qn, qq))
+    idx = (torch.as_tensor(qn), torch.as_tensor(qq))
+    _check_grads(w, (None, to_f64(go[idx]), to_f64(gz[idx]), to_f64(gr[idx])), (None, rgo, rgz, rgr),
+                 w.ref[qn, qq], w.offsets[qn, qq], check_gv=False)
+    # grad_value rows, through the oracle's core with the oracle's own locations and weights
+    rs = rng.integers(0, d["S"], 300)
+    rm = rng.integers(0, d["M"], 300)
+    rn = rng.integers(0, d["N"], 300)
+    loc = fused_locations(w.ref, w.offsets, w.spatial_shapes)
+    A = softmax_weights(w.logits)
+    rgv = msda_grad_value_rows(w.value, w.spatial_shapes, w.level_start, loc, A, w.grad_out, (rn, rs, rm))
+    assert_f32("grad_value", to_f64(gv[torch.as_tensor(rn), torch.as_tensor(rs), torch.as_tensor(rm)]), rgv)
+    # adjoint identity over the whole tensors: <G, out> = <grad_value, value>
+    lhs = float((g.double() * out.double()).sum())
+    rv = float((gv.double() * value.double()).sum())
+    scale = float((g.double().abs() * out.double().abs()).sum())
+    assert abs(lhs - rv) <= 1e-6 * scale, (lhs, rv, scale)
+    # the logit gradients of one head sum to zero (softmax is shift-invariant)
+    assert float(gz.double().sum(dim=(-2, -1)).abs().max()) <= 1e-5
+
+
+def test_fused_backward_without_grad_ref_and_determinism():
+    w = fused_workload("decoder", N=2, Lq=300, ref_dim=4, dtype="f32", seed=70, with_grad=True)
+    note("fused backward, grad_ref skipped vs computed, repeated calls")
+    a = _gpu_fused_backward(w)
+    b = _gpu_fused_backward(w, need_grad_ref=False)
+    assert b[3] is None
+    # grad_offsets, grad_logits and grad_ref do not depend on the order of work
+    np.testing.assert_array_equal(a[1], b[1])
+    np.testing.assert_array_equal(a[2], b[2])
+    c = _gpu_fused_backward(w)
+    np.testing.assert_array_equal(a[3], c[3])
+    assert max_abs(a[0], b[0]) <= 1e-6
+
+
+@pytest.mark.parametrize("L,K,D,dtype", [(16, 16, 8, "f32"), (3, 5, 5, "f32"), (2, 3, 100, "f32"),
+                                         (2, 4, 6, "bf16"), (1, 1, 64, "f32")])
+def test_fused_shapes(L, K, D, dtype):
+    shapes = [(9, 13), (5, 7), (3, 4), (2, 2)] * 4
+    w = fused_workload("decoder", N=1, shapes=shapes[:L], Lq=37, M=3, D=D, K=K, ref_dim=4 if L % 2 else 2,
+                       dtype=dtype, seed=80 + L + K, with_grad=True)
+    note(f"fused shapes L={L} K={K} D={D} {dtype}")
+    value, ref, off, logits, _ = _dev(w)
+    out = to_f64(msda.msda_fused_forward(value, w.spatial_shapes, w.level_start, ref, off, logits))
+    torch.cuda.synchronize()
+    _check_out(w, out, msda_fused_forward(*_oracle_args(w)))
+    got = _gpu_fused_backward(w)
+    _check_grads(w, got, msda_fused_backward(*_oracle_args(w), w.grad_out), w.ref, w.offsets)
+
+
+def test_fused_nan_logit_poisons_only_its_head():
+    w = fused_workload("decoder", N=1, shapes=((6, 8), (3, 4)), Lq=5, M=2, D=8, K=3, seed=90)
+    w.logits[0, 2, 1, 0, 1] = np.nan
+    note("fused forward with one NaN logit")
+    value, ref, off, logits, _ = _dev(w)
+    out = to_f64(msda.msda_fused_forward(value, w.spatial_shapes, w.level_start, ref, off, logits))
+    torch.cuda.synchronize()
+    ref_out = msda_fused_forward(*_oracle_args(w))
+    assert np.array_equal(np.isnan(out), np.isnan(ref_out))
+    assert np.isnan(out[0, 2, 1]).all() and np.isfinite(np.delete(out.reshape(-1, 8), 5, axis=0)).all()
+    keep = ~np.isnan(ref_out)
+    assert_f32("out", out[keep], ref_out[keep])
+
+
+def test_fused_autograd_wrapper():
+    w = fused_workload("decoder", N=1, shapes=((6, 8), (3, 4)), Lq=10, M=2, D=8, K=2, ref_dim=4, seed=95,
+                       with_grad=True)
+    value, ref, off, logits, g = _dev(w)
+    for t in (value, ref, off, logits):
+        t.requires_grad_(True)
+    note("fused autograd wrapper")
+    out = msda.msda_fused_sample(value, w.spatial_shapes, w.level_start, ref, off, logits)
+    out.backward(g)
+    gv, go, gz, gr = msda.msda_fused_backward(value.detach(), w.spatial_shapes, w.level_start, ref.detach(),
+                                              off.detach(), logits.detach(), g)
+    torch.cuda.synchronize()
+    assert torch.allclose(value.grad, gv, atol=1e-6)
+    assert torch.equal(off.grad, go) and torch.equal(logits.grad, gz) and torch.equal(ref.grad, gr)

@@ -498,3 +498,23 @@ def test_box_locations_are_one_rounding_of_the_fused_multiply_add():
                 assert got[0, q, 0, 0, 0, c] == round_fraction_to_f32(ex), (q, c)
     # the halfway cases do round up, away from the float64 sum's tie
     assert np.all(fused_locations(box, off, shapes)[0, :, 0, 0, 0, 0] == np.float32(1 + 2.0 ** -23))
+
+
+@pytest.mark.parametrize("ref_dim", [2, 4])
+def test_fused_backward_query_subset_agrees_with_full(ref_dim):
+    rng = np.random.default_rng(99 + ref_dim)
+    shapes = np.array([[6, 8], [3, 5]])
+    starts = np.array([0, 48])
+    N, Lq, M, D, L, K = 2, 5, 3, 4, 2, 2
+    value = rng.standard_normal((N, 63, M, D))
+    ref = rng.uniform(0.2, 0.8, (N, Lq, ref_dim)).astype(np.float32)
+    off = (rng.standard_normal((N, Lq, M, L, K, 2)) * (1.5 if ref_dim == 2 else 0.3)).astype(np.float32)
+    logits = rng.standard_normal((N, Lq, M, L, K)).astype(np.float32)
+    G = rng.standard_normal((N, Lq, M, D))
+    _, go, gz, gr = msda_fused_backward(value, shapes, starts, ref, off, logits, G)
+    qn, qq = np.array([1, 0, 1]), np.array([4, 2, 0])
+    gv, go_s, gz_s, gr_s = msda_fused_backward(value, shapes, starts, ref, off, logits, G, queries=(qn, qq))
+    assert gv is None
+    np.testing.assert_allclose(go_s, go[qn, qq], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(gz_s, gz[qn, qq], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(gr_s, gr[qn, qq], rtol=0, atol=1e-12)

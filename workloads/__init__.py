@@ -200,6 +200,79 @@ def uniform_workload(N=1, shapes=((16, 16),), Lq=32, M=2, D=8, K=4, dtype="f32",
                     meta=dict(seed=seed, recipe=f"locations U[{lo},{hi}]^2"))
 
 
+@dataclass
+class FusedWorkload:
+    """Raw predictions for the fused entry points: ref [N,Lq,2] reference points
+    (normalised x, y) or [N,Lq,4] boxes (cx, cy, w, h); offsets [N,Lq,M,L,K,2]
+    in level-l pixels (points) or in box units (boxes); logits [N,Lq,M,L,K];
+    all float32. value / grad_out as in Workload."""
+
+    name: str
+    dtype: str
+    value: np.ndarray
+    spatial_shapes: np.ndarray
+    level_start: np.ndarray
+    ref: np.ndarray
+    offsets: np.ndarray
+    logits: np.ndarray
+    grad_out: np.ndarray | None = None
+    value_bits: np.ndarray | None = None
+    grad_out_bits: np.ndarray | None = None
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def dims(self):
+        N, S, M, D = self.value.shape
+        _, Lq, _, L, K, _ = self.offsets.shape
+        return dict(N=N, S=S, M=M, D=D, L=L, Lq=Lq, K=K, ref_dim=self.ref.shape[-1])
+
+    @property
+    def points(self):
+        d = self.dims
+        return d["N"] * d["Lq"] * d["M"] * d["L"] * d["K"]
+
+
+def fused_workload(kind="encoder", N=1, shapes=COCO_LEVELS, Lq=300, M=8, D=32, K=4, dtype="f32", seed=8,
+                   ref_dim=2, offset_px=2.0, box_offset_sd=0.25, with_grad=False, name=None):
+    """Raw inputs of the step before the sampling core.
+
+    kind "encoder": every pixel is a query (Lq = S) with its pixel centre as
+    reference point (ref_dim 2) and N(0, offset_px) offsets in level pixels.
+    kind "decoder": Lq queries per image; points uniform in [0,1]^2 with
+    N(0, offset_px) pixel offsets, or (ref_dim 4) boxes with centres uniform in
+    [0.05, 0.95]^2 and sizes uniform in [0.02, 0.6], offsets N(0, box_offset_sd)
+    in box units. Logits are N(0,1). Draw order: value -> ref -> offsets ->
+    logits -> grad_out."""
+    shapes = tuple(tuple(int(v) for v in hw) for hw in shapes)
+    L = len(shapes)
+    starts, S = level_starts(shapes)
+    rng = np.random.default_rng(seed)
+    value, value_bits = _value(rng, (N, S, M, D), "normal", dtype)
+    if kind == "encoder":
+        if ref_dim != 2:
+            raise ValueError("encoder queries use reference points")
+        Lq = S
+        ref = np.empty((Lq, 2), dtype=np.float64)
+        for (h, w), s0 in zip(shapes, starts):
+            yy, xx = np.meshgrid(np.arange(h), np.arange(w), indexing="ij")
+            ref[s0:s0 + h * w, 0] = ((xx + 0.5) / w).ravel()
+            ref[s0:s0 + h * w, 1] = ((yy + 0.5) / h).ravel()
+        ref = np.broadcast_to(ref, (N, Lq, 2))
+    elif ref_dim == 2:
+        ref = rng.uniform(0.0, 1.0, (N, Lq, 2))
+    elif ref_dim == 4:
+        ref = np.concatenate([rng.uniform(0.05, 0.95, (N, Lq, 2)), rng.uniform(0.02, 0.6, (N, Lq, 2))], -1)
+    else:
+        raise ValueError(ref_dim)
+    sd = offset_px if ref_dim == 2 else box_offset_sd
+    offsets = (rng.standard_normal((N, Lq, M, L, K, 2)) * sd).astype(np.float32)
+    logits = rng.standard_normal((N, Lq, M, L, K)).astype(np.float32)
+    g, g_bits = _grad_out(rng, (N, Lq, M, D), dtype) if with_grad else (None, None)
+    return FusedWorkload(name or f"fused_{kind}_ref{ref_dim}", dtype, value, np.asarray(shapes, dtype=np.int64),
+                         starts, np.ascontiguousarray(ref, dtype=np.float32), offsets, logits, g, value_bits,
+                         g_bits, meta=dict(seed=seed, kind=kind, ref_dim=ref_dim))
+
+
 # The five workloads the library is measured and checked on, plus the K=8
 # backward variant (the glossary page "Deformable Attention" gives K as 4 or 8).
 def config_workload(name, **override):
