@@ -142,6 +142,63 @@ def decoder_latency(msda, torch, dev, layers=6, reps=20):
     return res
 
 
+def fused_passes(msda, torch, dev, steps, rotate):
+    """The same encoder shape fed with raw predictions (reference points, pixel
+    offsets, logits) through msda_fused_forward / msda_fused_backward, next to
+    the unfused route: a torch softmax and location pass, then msda_forward."""
+    import numpy as np
+
+    from workloads import COCO_LEVELS, fused_workload
+
+    w = fused_workload("encoder", N=1, shapes=COCO_LEVELS, K=4, seed=2, with_grad=True)
+    d = w.dims
+    ss, ls = w.spatial_shapes, w.level_start
+    size = torch.tensor([[hw[1], hw[0]] for hw in ss.tolist()], dtype=torch.float32, device=dev)
+    sets = []
+    for _ in range(rotate):
+        s = {"value": torch.from_numpy(w.value).to(dev), "ref": torch.from_numpy(w.ref).to(dev),
+             "off": torch.from_numpy(w.offsets).to(dev), "logits": torch.from_numpy(w.logits).to(dev),
+             "g": torch.from_numpy(w.grad_out).to(dev)}
+        s["out"] = torch.empty((d["N"], d["Lq"], d["M"], d["D"]), dtype=torch.float32, device=dev)
+        s["gv"] = torch.empty_like(s["value"])
+        s["go"] = torch.empty_like(s["off"])
+        s["gz"] = torch.empty_like(s["logits"])
+        s["gr"] = torch.empty_like(s["ref"])
+        s["ws"] = torch.empty(msda.msda_backward_workspace_size(ss, ls, d["N"], d["S"], d["M"], d["D"], d["L"],
+                                                                d["Lq"], d["K"]), dtype=torch.uint8, device=dev)
+        sets.append(s)
+
+    def fwd(s):
+        msda.msda_fused_forward(s["value"], ss, ls, s["ref"], s["off"], s["logits"], out=s["out"])
+
+    def bwd(s):
+        msda.msda_fused_backward(s["value"], ss, ls, s["ref"], s["off"], s["logits"], s["g"], grad_value=s["gv"],
+                                 grad_offsets=s["go"], grad_logits=s["gz"], grad_ref=s["gr"], workspace=s["ws"])
+
+    def unfused_fwd(s):
+        attn = torch.softmax(s["logits"].reshape(d["N"], d["Lq"], d["M"], -1), -1).reshape(s["logits"].shape)
+        loc = s["ref"][:, :, None, None, None, :] + s["off"] / size[None, None, None, :, None, :]
+        msda.msda_forward(s["value"], ss, ls, loc, attn, out=s["out"])
+
+    stream = torch.cuda.current_stream()
+    res = {"workload": "encoder shape as above from raw inputs: reference points at pixel centres, "
+                       "N(0,2px) offsets, N(0,1) logits"}
+    for name, fn in (("fwd", fwd), ("bwd", bwd), ("unfused_fwd", unfused_fwd)):
+        for i in range(3):
+            fn(sets[i % rotate])
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for i in range(steps):
+            ev[i][0].record(stream)
+            fn(sets[i % rotate])
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        ms = np.array([a.elapsed_time(b) for a, b in ev])
+        res[name] = {"us_mean": round(float(ms.mean()) * 1e3, 2), "us_median": round(float(np.median(ms)) * 1e3, 2),
+                     "points_per_s": w.points / (float(ms.mean()) * 1e-3)}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -266,6 +323,7 @@ def main():
         "kernel_source_sha256": kernel_source_hash(),
     }
     result["decoder_latency"] = decoder_latency(msda, torch, dev)
+    result["fused_inputs"] = fused_passes(msda, torch, dev, min(args.steps, 30), args.rotate)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)

@@ -109,8 +109,8 @@ msda_status msda_forward(const void *value, const int64_t *spatial_shapes,
  * these sizes (the same checks as msda_validate apply). The workspace holds a
  * counting sort of the samples by the 8x8-pixel tile of the value map they
  * touch: a few counters per tile plus up to four 16-byte entries per sample,
- * and 24 bytes per (image, query, head) for the fused variant, about
- * 64*N*Lq*M*L*K + 24*N*Lq*M bytes.
+ * and 16 bytes per (image, query, head) for the fused variant, about
+ * 64*N*Lq*M*L*K + 16*N*Lq*M bytes.
  */
 msda_status msda_backward_workspace_size(const int64_t *spatial_shapes, const int64_t *level_start,
                                          int64_t N, int64_t S, int64_t M, int64_t D, int64_t L,

@@ -131,7 +131,6 @@ msda_status backward_impl(const void *value, const int64_t *spatial_shapes, cons
   p.ws.n_work = reinterpret_cast<uint32_t *>(ws + wl.off_nwork);
   p.ws.split_list = reinterpret_cast<uint32_t *>(ws + wl.off_split);
   p.ws.entries = reinterpret_cast<uint32_t *>(ws + wl.off_entries);
-  p.ws.stats = reinterpret_cast<float *>(ws + wl.off_stats);
   p.ws.ref_part = reinterpret_cast<float *>(ws + wl.off_refpart);
   for (int64_t n0 = 0; n0 < N; n0 += step) {
     const int64_t nb = std::min(step, N - n0);

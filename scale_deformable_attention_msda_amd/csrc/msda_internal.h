@@ -49,7 +49,6 @@ struct Workspace {
   uint32_t *n_work;       // [1]
   uint32_t *split_list;   // [T] tiles whose entries span several work items
   uint32_t *entries;      // [4*Emax] (sample, tile) entries, tile-major, 16-byte records
-  float *stats;           // [2*pairs] softmax max and 1/sum of each pair's logits (fused inputs)
   float *ref_part;        // [4*pairs] per-pair sums of the reference gradient (fused inputs)
 };
 
@@ -74,7 +73,11 @@ struct Params {
   int32_t qpb;           // queries per workgroup of the binning passes
   int32_t gvec;          // grad_out rows allow 16-byte loads
   int32_t gv_blocks;     // grad_value blocks of the fused backward launch
-  int32_t sparse;        // grad_value zero-filled first; empty tiles get no work
+  int32_t scatter;       // grad_value zero-filled, then added to with float atomics per sample
+                         // (sparse launches: no tile sort)
+  int32_t seg_softmax;   // fused inputs: a pair's L*K logits sit in L*K consecutive lanes of
+                         // the per-sample passes (L*K a power of two <= 64, one chunk)
+  int32_t ref_inblock;   // fused inputs: every workgroup holds whole queries (all M heads)
   // Fused inputs (ref_dim 2 or 4): loc then holds offsets, attn holds logits,
   // and grad_loc / grad_attn receive the offset and logit gradients.
   // ref_dim 0: loc and attn are the sampling core's own inputs.
@@ -101,8 +104,7 @@ LaunchShape choose_shape(int D, DType dt, uintptr_t align_bits, int64_t pairs);
 // Tile table and workspace layout of a launch covering `nimg` images.
 struct WorkspaceLayout {
   int64_t T, Wmax, Emax;
-  size_t off_count, off_cursor, off_start, off_witem, off_nwork, off_split, off_entries, off_stats,
-      off_refpart, bytes;
+  size_t off_count, off_cursor, off_start, off_witem, off_nwork, off_split, off_entries, off_refpart, bytes;
 };
 WorkspaceLayout workspace_layout(const int64_t *spatial_shapes, int64_t L, int64_t nimg, int64_t M,
                                  int64_t Lq, int64_t K);

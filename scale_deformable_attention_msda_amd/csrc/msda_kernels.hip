@@ -268,6 +268,15 @@ __device__ __forceinline__ float2 pair_softmax_stats(const float *z, bool active
   return make_float2(mx, 1.0f / s);
 }
 
+// Softmax weight of logit z when the L*K logits of its pair sit in lk
+// consecutive lanes aligned to lk (a power of two <= 64, all of them active):
+// the maximum and the sum come from lane exchanges, with no memory traffic.
+__device__ __forceinline__ float segment_softmax(float z, int lk) {
+  const float mx = group_sum<0, true>(z, lk);
+  const float e = expf(z - mx);
+  return e * (1.0f / group_sum<0>(e, lk));
+}
+
 // ---------------------------------------------------------------- forward
 
 struct __align__(16) FDesc {
@@ -298,8 +307,10 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(const Params p) {
   if (tid < npairs) pbase[tid] = pair_base(p, (uint32_t)(P0 + tid));
   if constexpr (FUSE) {
     if (tid < npairs) sref[tid] = load_ref(p, (uint32_t)(P0 + tid));
-    const float2 st = pair_softmax_stats<LPP>(p.attn + (active ? (P0 + g) * p.LK : 0), active, j, lpp, p.LK);
-    if (active && j == 0) sst[g] = st;
+    if (!p.seg_softmax) {
+      const float2 st = pair_softmax_stats<LPP>(p.attn + (active ? (P0 + g) * p.LK : 0), active, j, lpp, p.LK);
+      if (active && j == 0) sst[g] = st;
+    }
   }
   const uint32_t kmg = small_magic((uint32_t)p.K);
 
@@ -334,7 +345,7 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(const Params p) {
       float A = z;
       if constexpr (FUSE) {
         xy = form_loc<true>(p, v, l, sref[gg], sH, sW);
-        A = softmax_weight(z, sst[gg]);
+        A = p.seg_softmax ? segment_softmax(z, p.LK) : softmax_weight(z, sst[gg]);
       }
       const Sample s = sample_geometry(p, pbase[gg], xy, A, l, sH, sW, sS);
       FDesc d;
@@ -401,31 +412,36 @@ struct __align__(16) BDesc {
 };
 
 constexpr size_t kSampleSmemPlain =
-    kDescCap * sizeof(BDesc) + kDescCap * sizeof(float3) + 3 * kMaxLevels * 4 + kBlock * 4;
+    kDescCap * (sizeof(BDesc) + sizeof(float3) + 4) + 3 * kMaxLevels * 4 + kBlock * 4;
 // fused inputs add per pair: reference, softmax statistics, sum of A * grad_attn;
-// per staged sample: its weight and its offset
-constexpr size_t kSampleSmemFused = kSampleSmemPlain + kBlock * (16 + 8 + 4) + kDescCap * (4 + 8);
+// per staged sample: its offset
+constexpr size_t kSampleSmemFused = kSampleSmemPlain + kBlock * (16 + 8 + 4) + kDescCap * 8;
 template <bool FUSE>
 constexpr size_t sample_smem() { return FUSE ? kSampleSmemFused : kSampleSmemPlain; }
 
 // grad_attn and grad_loc of the pairs of logical block `block` (of `nblocks`),
-// with LDS carved from `smem` (sample_smem<FUSE>() bytes). With fused inputs
-// they become the logit and offset gradients: through the softmax,
+// with LDS carved from `smem` (sample_smem<FUSE>() bytes). With p.scatter the
+// same pass also adds each sample's grad_value contributions (attn * corner
+// weight * grad_out) with float atomics. With fused inputs grad_attn and
+// grad_loc become the logit and offset gradients: through the softmax,
 // d/dz_i = A_i (grad_attn_i - sum_j A_j grad_attn_j); through the location,
 // d/d offset = grad_loc / size (points) or grad_loc * box size (boxes); and the
-// pair's sums for the reference gradient go to the workspace.
+// reference gradient is the sum of grad_loc (and of grad_loc * offset for the
+// box size) over a query's samples.
 template <typename T, int VEC, int NCG, int LPP, bool FUSE>
 __device__ __forceinline__ void bwd_sample_body(const Params &p, int block, int nblocks, unsigned char *smem) {
   BDesc *desc = reinterpret_cast<BDesc *>(smem);
-  float3 *res = reinterpret_cast<float3 *>(smem + kDescCap * sizeof(BDesc));
-  int32_t *sH = reinterpret_cast<int32_t *>(smem + kDescCap * (sizeof(BDesc) + sizeof(float3)));
+  float3 *res = reinterpret_cast<float3 *>(desc + kDescCap);
+  float *sA = reinterpret_cast<float *>(res + kDescCap);  // each staged sample's weight
+  int32_t *sH = reinterpret_cast<int32_t *>(sA + kDescCap);
   int32_t *sW = sH + kMaxLevels, *sS = sW + kMaxLevels;
   uint32_t *pbase = reinterpret_cast<uint32_t *>(sS + kMaxLevels);
-  float4 *sref = reinterpret_cast<float4 *>(smem + kSampleSmemPlain);  // used with FUSE only
+  // fused inputs only
+  float4 *sref = reinterpret_cast<float4 *>(smem + kSampleSmemPlain);
   float2 *sst = reinterpret_cast<float2 *>(sref + kBlock);
-  float *ssum = reinterpret_cast<float *>(sst + kBlock);
-  float *sA = ssum + kBlock;
-  float2 *soff = reinterpret_cast<float2 *>(sA + kDescCap);
+  float2 *soff = reinterpret_cast<float2 *>(sst + kBlock);
+  float *ssum = reinterpret_cast<float *>(soff + kDescCap);
+  float4 *sgr = reinterpret_cast<float4 *>(smem);  // reuses desc once the last chunk is done
   load_levels(p, sH, sW, sS);
 
   const int tid = threadIdx.x;
@@ -439,9 +455,10 @@ __device__ __forceinline__ void bwd_sample_body(const Params &p, int block, int 
   const bool active = g < npairs;
   if (tid < npairs) pbase[tid] = pair_base(p, (uint32_t)(P0 + tid));
   if constexpr (FUSE) {
-    if (tid < npairs) {
-      sref[tid] = load_ref(p, (uint32_t)(P0 + tid));
-      sst[tid] = *reinterpret_cast<const float2 *>(p.ws.stats + 2 * (P0 + tid));
+    if (tid < npairs) sref[tid] = load_ref(p, (uint32_t)(P0 + tid));
+    if (!p.seg_softmax) {
+      const float2 st = pair_softmax_stats<LPP>(p.attn + (active ? (P0 + g) * p.LK : 0), active, j, lpp, p.LK);
+      if (active && j == 0) sst[g] = st;
     }
   }
   // the pair's sums over its samples (identical in all its lanes)
@@ -450,6 +467,7 @@ __device__ __forceinline__ void bwd_sample_body(const Params &p, int block, int 
 
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.value, p.value_elems * (uint32_t)T::size);
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.grad_out, (uint32_t)(p.pairs * p.D) * (uint32_t)T::size);
+  const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.grad_value, p.value_elems * 4u);
   const int nvec = p.D / VEC;
   uint32_t lane_elem[NCG];
   float G[NCG][VEC];
@@ -477,11 +495,12 @@ __device__ __forceinline__ void bwd_sample_body(const Params &p, int block, int 
       float A = z;
       if constexpr (FUSE) {
         xy = form_loc<true>(p, v, l, sref[gg], sH, sW);
-        A = softmax_weight(z, sst[gg]);
-        // the softmax gradient needs every sample's weight, in the map or not
-        sA[pp * dstride + gg] = A;
+        A = p.seg_softmax ? segment_softmax(z, p.LK) : softmax_weight(z, sst[gg]);
         soff[pp * dstride + gg] = v;
       }
+      // the weight itself, in the map or not (the softmax gradient needs it;
+      // corners outside the map drop the scatter's atomics)
+      sA[pp * dstride + gg] = A;
       const Sample s = sample_geometry(p, pbase[gg], xy, A, l, sH, sW, sS);
       BDesc d;
 #pragma unroll
@@ -509,6 +528,20 @@ __device__ __forceinline__ void bwd_sample_body(const Params &p, int block, int 
           }
         }
         const float a = d.a, b = d.b;
+        if (p.scatter) {
+          const float A = sA[pp * dstride + g];
+          const float wa[2] = {1.0f - a, a}, wb[2] = {1.0f - b, b};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float wc = A * wb[c >> 1] * wa[c & 1];
+#pragma unroll
+            for (int cg = 0; cg < NCG; ++cg)
+#pragma unroll
+              for (int e = 0; e < VEC; ++e)
+                __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(
+                    wc * G[cg][e], rg, (int)((d.off[c] + lane_elem[cg] + (uint32_t)e) * 4u), 0, 0);
+          }
+        }
         float ga = (1.0f - b) * ((1.0f - a) * dot[0] + a * dot[1]) + b * ((1.0f - a) * dot[2] + a * dot[3]);
         float gx = (1.0f - b) * (dot[1] - dot[0]) + b * (dot[3] - dot[2]);
         float gy = (1.0f - a) * (dot[2] - dot[0]) + a * (dot[3] - dot[1]);
@@ -526,6 +559,9 @@ __device__ __forceinline__ void bwd_sample_body(const Params &p, int block, int 
           acc_by = fmaf(gly, o.y, acc_by);
         }
       }
+      if constexpr (FUSE) {
+        if (j == 0) ssum[g] = acc_s;  // the pair's full sum after its last chunk
+      }
     }
     __syncthreads();
     for (int i = tid; i < npairs * pcn; i += kBlock) {
@@ -533,9 +569,12 @@ __device__ __forceinline__ void bwd_sample_body(const Params &p, int block, int 
       const int pp = i - gg * pcn;
       const float3 r = res[pp * dstride + gg];
       const int64_t gi = (P0 + gg) * p.LK + pc0 + pp;
-      p.grad_attn[gi] = r.x;  // fused inputs: finished below, once the pair's sum is known
       float2 gl = make_float2(r.y, r.z);
+      float gz = r.x;
       if constexpr (FUSE) {
+        // one chunk holds all of the pair's samples: its sum is complete here;
+        // otherwise grad_attn is stored and finished below
+        if (p.LK <= p.pc) gz = sA[pp * dstride + gg] * (r.x - ssum[gg]);
         if (p.ref_dim == 2) {
           const int l = (pc0 + pp) / p.K;
           gl = make_float2(r.y / (float)sW[l], r.z / (float)sH[l]);
@@ -544,23 +583,42 @@ __device__ __forceinline__ void bwd_sample_body(const Params &p, int block, int 
           gl = make_float2(r.y * rf.z, r.z * rf.w);
         }
       }
+      p.grad_attn[gi] = gz;
       *reinterpret_cast<float2 *>(p.grad_loc + 2 * gi) = gl;
     }
   }
   if constexpr (FUSE) {
-    if (active && j == 0) {
-      ssum[g] = acc_s;
-      if (p.grad_ref)
-        *reinterpret_cast<float4 *>(p.ws.ref_part + 4 * (P0 + g)) = make_float4(acc_rx, acc_ry, acc_bx, acc_by);
+    const bool inblock = p.grad_ref && p.ref_inblock;
+    if (active && j == 0 && p.grad_ref) {
+      const float4 part = make_float4(acc_rx, acc_ry, acc_bx, acc_by);
+      if (inblock)
+        sgr[g] = part;
+      else
+        *reinterpret_cast<float4 *>(p.ws.ref_part + 4 * (P0 + g)) = part;
     }
-    __syncthreads();
-    // grad_logits from this block's grad_attn values (written above by the
-    // block itself and visible after the barrier)
-    for (int i = tid; i < npairs * p.LK; i += kBlock) {
-      const int gg = i / p.LK;
-      const int64_t gi = P0 * p.LK + i;
-      const float A = softmax_weight(p.attn[gi], sst[gg]);
-      p.grad_attn[gi] = A * (p.grad_attn[gi] - ssum[gg]);
+    if (p.LK > p.pc || inblock) __syncthreads();
+    if (p.LK > p.pc) {
+      // grad_logits from the grad_attn values this block stored above
+      // (visible to the whole workgroup after the barrier)
+      for (int i = tid; i < npairs * p.LK; i += kBlock) {
+        const int gg = i / p.LK;
+        const int64_t gi = P0 * p.LK + i;
+        const float A = softmax_weight(p.attn[gi], sst[gg]);
+        p.grad_attn[gi] = A * (p.grad_attn[gi] - ssum[gg]);
+      }
+    }
+    if (inblock) {
+      // the block holds whole queries: sum the M pairs of each, in head order
+      const int nq = npairs / p.M;
+      for (int i = tid; i < nq * p.ref_dim; i += kBlock) {
+        const int qi = i / p.ref_dim, c = i - qi * p.ref_dim;
+        float sum = 0.0f;
+        for (int m = 0; m < p.M; ++m) {
+          const float4 v = sgr[qi * p.M + m];
+          sum += c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w;
+        }
+        p.grad_ref[(P0 / p.M + qi) * p.ref_dim + c] = sum;
+      }
     }
   }
 }
@@ -629,6 +687,9 @@ template <int MODE, bool FUSE>
 __global__ __launch_bounds__(kBlock) void bin_kernel(const Params p) {
   __shared__ uint32_t cnt[kBinCap];
   __shared__ uint32_t gbase[MODE == 1 ? kBinCap : 1];
+  // softmax statistics of the block's pairs when L*K is not a power of two:
+  // then L*K >= 3, so a block holds at most 1024 / 3 pairs
+  __shared__ float2 bst[MODE == 1 && FUSE ? 1024 / 3 + 1 : 1];
   __shared__ int32_t sH[kMaxLevels], sW[kMaxLevels], sS[kMaxLevels], sTW[kMaxLevels], sToff[kMaxLevels];
   load_tile_levels(p, sH, sW, sS, sTW, sToff);
   const int tid = threadIdx.x;
@@ -650,16 +711,23 @@ __global__ __launch_bounds__(kBlock) void bin_kernel(const Params p) {
   uint4 *rec_out = reinterpret_cast<uint4 *>(p.ws.entries);
   if (local)
     for (int i = tid; i < p.TPI; i += kBlock) cnt[i] = 0;
-  if constexpr (FUSE && MODE == 0) {
-    // softmax statistics of the workgroup's pairs, read by the later passes
-    for (int qi = tid; qi < nsamp / p.LK; qi += kBlock) {
-      const int64_t P = ((int64_t)n * p.Lq + q0 + qi) * p.M + m;
-      const float *z = p.attn + P * p.LK;
-      float mx = -INFINITY;
-      for (int i = 0; i < p.LK; ++i) mx = max_nan(mx, z[i]);
-      float sum = 0.0f;
-      for (int i = 0; i < p.LK; ++i) sum += expf(z[i] - mx);
-      *reinterpret_cast<float2 *>(p.ws.stats + 2 * P) = make_float2(mx, 1.0f / sum);
+  // Weights from logits (fused inputs): a pair's L*K samples are consecutive
+  // lanes here, so a power-of-two L*K up to 64 takes its softmax from lane
+  // exchanges; otherwise the block's pairs get their statistics first, ls
+  // lanes per pair.
+  const bool seg = (p.LK & (p.LK - 1)) == 0 && p.LK <= 64;
+  if constexpr (FUSE && MODE == 1) {
+    if (!seg) {
+      const int nq = nsamp / p.LK;
+      int ls = 1;
+      while (ls < 64 && 2 * ls * nq <= kBlock) ls *= 2;
+      for (int base = 0; base < nq; base += kBlock / ls) {
+        const int qi = base + tid / ls;
+        const bool act = qi < nq;
+        const int64_t P = ((int64_t)n * p.Lq + q0 + (act ? qi : 0)) * p.M + m;
+        const float2 st = pair_softmax_stats<0>(p.attn + P * p.LK, act, tid % ls, ls, p.LK);
+        if (act && tid % ls == 0) bst[qi] = st;
+      }
     }
   }
   __syncthreads();
@@ -682,13 +750,15 @@ __global__ __launch_bounds__(kBlock) void bin_kernel(const Params p) {
     const int l = pt / p.K;
     float2 xy = *reinterpret_cast<const float2 *>(p.loc + 2 * sid);
     if constexpr (FUSE) xy = form_loc<true>(p, xy, l, load_ref(p, P), sH, sW);
+    float A = 0.0f;
+    if constexpr (MODE == 1) {
+      A = p.attn[sid];
+      // before the branch below: every lane of the pair takes part
+      if constexpr (FUSE) A = seg ? segment_softmax(A, p.LK) : softmax_weight(A, bst[qi]);
+    }
     Footprint f;
     if (!sample_footprint(xy.x, xy.y, sH[l], sW[l], f)) continue;
-    if (MODE == 1) {
-      float A = p.attn[sid];
-      if constexpr (FUSE) A = softmax_weight(A, *reinterpret_cast<const float2 *>(p.ws.stats + 2 * (int64_t)P));
-      rec[r] = make_uint4(P, __float_as_uint(f.x), __float_as_uint(f.y), __float_as_uint(A));
-    }
+    if (MODE == 1) rec[r] = make_uint4(P, __float_as_uint(f.x), __float_as_uint(f.y), __float_as_uint(A));
     // tile rows/columns touched by the in-map corners
     const int ya = f.r0 ? f.y0 : f.y0 + 1, yb = f.r1 ? f.y0 + 1 : f.y0;
     const int xa = f.c0 ? f.x0 : f.x0 + 1, xb = f.c1 ? f.x0 + 1 : f.x0;
@@ -737,17 +807,16 @@ __global__ __launch_bounds__(kBlock) void bin_kernel(const Params p) {
 
 // Exclusive scan of the tile counts (one workgroup of 1024 threads, each
 // owning a run of consecutive tiles) and the list of grad_value work items:
-// a tile gives ceil(count / kPartEntries) items, at least one unless the
-// launch is sparse (grad_value zero-filled beforehand, empty tiles skipped).
-// Tiles with several items are listed so that they can be zeroed first.
+// a tile gives ceil(count / kPartEntries) items, at least one (an empty tile's
+// item writes its zeros). Tiles with several items are listed so that they can
+// be zeroed first.
 __global__ __launch_bounds__(1024) void scan_kernel(const Params p) {
   __shared__ uint32_t wsum_c[16], wsum_p[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int per = (p.T + 1023) / 1024;
   const int t0 = tid * per, t1 = min(p.T, t0 + per);
   auto parts_of = [&](uint32_t c) -> uint32_t {
-    const uint32_t q = (c + kPartEntries - 1) / kPartEntries;
-    return p.sparse ? q : max(1u, q);
+    return max(1u, (c + kPartEntries - 1) / kPartEntries);
   };
   uint32_t rc = 0, rp = 0;
   for (int t = t0; t < t1; ++t) {
@@ -786,7 +855,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(const Params p) {
     const uint32_t parts = parts_of(c);
     p.ws.tile_start[t] = start;
     p.ws.tile_cursor[t] = start;
-    if (parts > 1 && !p.sparse) p.ws.split_list[atomicAdd(p.ws.tile_count + p.T, 1u)] = (uint32_t)t;
+    if (parts > 1) p.ws.split_list[atomicAdd(p.ws.tile_count + p.T, 1u)] = (uint32_t)t;
     // Items are stored last tile first: each (head, image) block of tiles
     // ends with the coarse levels, whose crowded tiles then start first.
     for (uint32_t k = 0; k < parts; ++k) {
@@ -1111,13 +1180,23 @@ hipError_t launch_fn(const void *fn, int64_t blocks, int threads, int gy, Params
   return hipLaunchKernel(fn, dim3((unsigned)blocks, (unsigned)gy), dim3(threads), args, 0, stream);
 }
 
+// Lane mapping and chunking of the per-sample passes (forward and the
+// backward's sample gradients).
+void set_sample_shape(Params &p, const LaunchShape &s) {
+  p.lpp = s.lpp;
+  const int ppb = kBlock / s.lpp;
+  p.pc = min(p.LK, max(1, kDescCap / (ppb + 1)));
+  const bool pow2 = (p.LK & (p.LK - 1)) == 0;
+  p.seg_softmax = p.ref_dim != 0 && pow2 && p.LK <= 64 && p.LK <= p.pc ? 1 : 0;
+  p.ref_inblock = ppb % p.M == 0 ? 1 : 0;
+}
+
 hipError_t launch_pairs(bool fwd, const Params &p_in, DType dt, const LaunchShape &s, hipStream_t stream) {
   KernelFn fn = select(fwd, p_in.ref_dim != 0, dt, s);
   if (!fn) return hipErrorInvalidValue;
   Params p = p_in;
-  p.lpp = s.lpp;
+  set_sample_shape(p, s);
   const int ppb = kBlock / s.lpp;
-  p.pc = min(p.LK, max(1, kDescCap / (ppb + 1)));
   const int64_t blocks = (p.pairs + ppb - 1) / ppb;
   return launch_fn(reinterpret_cast<const void *>(fn), blocks, kBlock, 1, p, stream);
 }
@@ -1191,8 +1270,7 @@ WorkspaceLayout workspace_layout(const int64_t *spatial_shapes, int64_t L, int64
   w.off_nwork = o;   o = up(o + 4);
   w.off_split = o;   o = up(o + 4 * (size_t)w.T);
   w.off_entries = o; o = up(o + 16 * (size_t)w.Emax);
-  // fused inputs: softmax statistics and reference-gradient sums per pair
-  w.off_stats = o;   o = up(o + 8 * (size_t)(nimg * Lq * M));
+  // fused inputs: reference-gradient sums per pair
   w.off_refpart = o; o = up(o + 16 * (size_t)(nimg * Lq * M));
   w.bytes = o;
   return w;
@@ -1205,70 +1283,72 @@ hipError_t launch_forward(const Params &p, DType dt, const LaunchShape &s, hipSt
 hipError_t launch_backward(const Params &p_in, DType dt, const LaunchShape &s, hipStream_t stream) {
   Params p = p_in;
   p.qpb = max(1, 1024 / p.LK);
-  p.lpp = s.lpp;
-  // Sparse launches (few samples per value tile, e.g. decoder queries):
-  // zero-fill grad_value once and give work only to tiles with entries.
-  p.sparse = (int64_t)p.Lq * p.LK < 32 * (int64_t)p.TPI ? 1 : 0;
-  if (p.sparse) {
-    hipError_t ez = launch_zero(p.grad_value, (int64_t)p.N * p.S * p.M * p.D, stream);
-    if (ez != hipSuccess) return ez;
-  }
-  // 16-byte grad_out loads in the grad_value pass when rows and pointer allow
-  p.gvec = (s.vec * (dt == DType::F32 ? 4 : 2)) == 16 ? 1 : 0;
-  hipError_t e;
-  // 1. tile counters and the split-tile counter
-  {
-    uint32_t *ptr = p.ws.tile_count;
-    int64_t n = p.T + 8;
-    void *args[] = {&ptr, &n};
-    e = hipLaunchKernel(reinterpret_cast<const void *>(zero_u32_kernel), dim3((unsigned)((n + kBlock - 1) / kBlock)),
-                        dim3(kBlock), args, 0, stream);
-    if (e != hipSuccess) return e;
-  }
-  // 2. counting sort of (sample, tile) entries; the scatter launch also clears
-  //    the tiles whose grad_value is summed over several work items
+  set_sample_shape(p, s);
   const bool fuse = p.ref_dim != 0;
-  const int64_t bin_blocks = (int64_t)p.N * p.M * ((p.Lq + p.qpb - 1) / p.qpb);
-  const void *bin0 = fuse ? reinterpret_cast<const void *>(bin_kernel<0, true>)
-                          : reinterpret_cast<const void *>(bin_kernel<0, false>);
-  const void *bin1 = fuse ? reinterpret_cast<const void *>(bin_kernel<1, true>)
-                          : reinterpret_cast<const void *>(bin_kernel<1, false>);
-  if ((e = launch_fn(bin0, bin_blocks, kBlock, 1, p, stream)) != hipSuccess) return e;
-  if ((e = launch_fn(reinterpret_cast<const void *>(scan_kernel), 1, 1024, 1, p, stream)) != hipSuccess) return e;
-  if ((e = launch_fn(bin1, bin_blocks + 256, kBlock, 1, p, stream)) != hipSuccess) return e;
-  // 3. grad_value per tile, and grad_attn / grad_loc per sample
-  const int64_t wmax = p.T + (4 * p.pairs * p.LK + kPartEntries - 1) / kPartEntries;
-  const int Dc = min(kChanGroup, p.D);
-  const int cs_need = (Dc + 3) / 4;
-  int cs = 1;
-  while (cs < cs_need) cs *= 2;
-  const int groups = (p.D + kChanGroup - 1) / kChanGroup;
-  const int ppb = kBlock / s.lpp;
-  p.pc = min(p.LK, max(1, kDescCap / (ppb + 1)));
-  const int64_t sample_blocks = (p.pairs + ppb - 1) / ppb;
-  const bool hot_f32 = dt == DType::F32 && s.vec == 4 && s.lpp == 8 && s.ncg == 1 && cs == 8;
-  const bool hot_bf16 = dt == DType::BF16 && s.vec == 8 && s.lpp == 4 && s.ncg == 1 && cs == 8;
-  // grad_value blocks rounded to a multiple of 8 so that the sample blocks'
-  // XCD-aware renumbering sees the hardware's block % 8 placement
-  const int64_t gvb = (wmax + 7) & ~(int64_t)7;
-  if ((hot_f32 || hot_bf16) && groups == 1 && gvb + sample_blocks <= 0x7fffffff) {
-    p.gv_blocks = (int32_t)gvb;
-    const void *fn;
-    if (hot_f32)
-      fn = fuse ? reinterpret_cast<const void *>(bwd_fused_kernel<F32, 4, 1, 8, 8, true>)
-                : reinterpret_cast<const void *>(bwd_fused_kernel<F32, 4, 1, 8, 8, false>);
-    else
-      fn = fuse ? reinterpret_cast<const void *>(bwd_fused_kernel<BF16, 8, 1, 4, 8, true>)
-                : reinterpret_cast<const void *>(bwd_fused_kernel<BF16, 8, 1, 4, 8, false>);
-    if ((e = launch_fn(fn, gvb + sample_blocks, kBlock, 1, p, stream)) != hipSuccess) return e;
-  } else {
+  hipError_t e;
+  // Sparse launches (few samples per 8x8 value tile, e.g. decoder queries): a
+  // tile sort would cost more than it saves; grad_value is zero-filled and
+  // the sample pass adds each corner's contribution with float atomics.
+  p.scatter = (int64_t)p.Lq * p.LK < 32 * (int64_t)p.TPI ? 1 : 0;
+  if (p.scatter) {
+    if ((e = launch_zero(p.grad_value, (int64_t)p.N * p.S * p.M * p.D, stream)) != hipSuccess) return e;
     if ((e = launch_pairs(false, p, dt, s, stream)) != hipSuccess) return e;
-    KernelFn gv = dt == DType::F32 ? pick_gv<F32>(cs) : pick_gv<BF16>(cs);
-    if ((e = launch_fn(reinterpret_cast<const void *>(gv), wmax, kBlock, groups, p, stream)) != hipSuccess)
-      return e;
+  } else {
+    // 16-byte grad_out loads in the grad_value pass when rows and pointer allow
+    p.gvec = (s.vec * (dt == DType::F32 ? 4 : 2)) == 16 ? 1 : 0;
+    // 1. tile counters and the split-tile counter
+    {
+      uint32_t *ptr = p.ws.tile_count;
+      int64_t n = p.T + 8;
+      void *args[] = {&ptr, &n};
+      e = hipLaunchKernel(reinterpret_cast<const void *>(zero_u32_kernel),
+                          dim3((unsigned)((n + kBlock - 1) / kBlock)), dim3(kBlock), args, 0, stream);
+      if (e != hipSuccess) return e;
+    }
+    // 2. counting sort of (sample, tile) entries; the scatter launch also clears
+    //    the tiles whose grad_value is summed over several work items
+    const int64_t bin_blocks = (int64_t)p.N * p.M * ((p.Lq + p.qpb - 1) / p.qpb);
+    const void *bin0 = fuse ? reinterpret_cast<const void *>(bin_kernel<0, true>)
+                            : reinterpret_cast<const void *>(bin_kernel<0, false>);
+    const void *bin1 = fuse ? reinterpret_cast<const void *>(bin_kernel<1, true>)
+                            : reinterpret_cast<const void *>(bin_kernel<1, false>);
+    if ((e = launch_fn(bin0, bin_blocks, kBlock, 1, p, stream)) != hipSuccess) return e;
+    if ((e = launch_fn(reinterpret_cast<const void *>(scan_kernel), 1, 1024, 1, p, stream)) != hipSuccess) return e;
+    if ((e = launch_fn(bin1, bin_blocks + 256, kBlock, 1, p, stream)) != hipSuccess) return e;
+    // 3. grad_value per tile, and grad_attn / grad_loc per sample
+    const int64_t wmax = p.T + (4 * p.pairs * p.LK + kPartEntries - 1) / kPartEntries;
+    const int Dc = min(kChanGroup, p.D);
+    const int cs_need = (Dc + 3) / 4;
+    int cs = 1;
+    while (cs < cs_need) cs *= 2;
+    const int groups = (p.D + kChanGroup - 1) / kChanGroup;
+    const int ppb = kBlock / s.lpp;
+    const int64_t sample_blocks = (p.pairs + ppb - 1) / ppb;
+    const bool hot_f32 = dt == DType::F32 && s.vec == 4 && s.lpp == 8 && s.ncg == 1 && cs == 8;
+    const bool hot_bf16 = dt == DType::BF16 && s.vec == 8 && s.lpp == 4 && s.ncg == 1 && cs == 8;
+    // grad_value blocks rounded to a multiple of 8 so that the sample blocks'
+    // XCD-aware renumbering sees the hardware's block % 8 placement
+    const int64_t gvb = (wmax + 7) & ~(int64_t)7;
+    if ((hot_f32 || hot_bf16) && groups == 1 && gvb + sample_blocks <= 0x7fffffff) {
+      p.gv_blocks = (int32_t)gvb;
+      const void *fn;
+      if (hot_f32)
+        fn = fuse ? reinterpret_cast<const void *>(bwd_fused_kernel<F32, 4, 1, 8, 8, true>)
+                  : reinterpret_cast<const void *>(bwd_fused_kernel<F32, 4, 1, 8, 8, false>);
+      else
+        fn = fuse ? reinterpret_cast<const void *>(bwd_fused_kernel<BF16, 8, 1, 4, 8, true>)
+                  : reinterpret_cast<const void *>(bwd_fused_kernel<BF16, 8, 1, 4, 8, false>);
+      if ((e = launch_fn(fn, gvb + sample_blocks, kBlock, 1, p, stream)) != hipSuccess) return e;
+    } else {
+      if ((e = launch_pairs(false, p, dt, s, stream)) != hipSuccess) return e;
+      KernelFn gv = dt == DType::F32 ? pick_gv<F32>(cs) : pick_gv<BF16>(cs);
+      if ((e = launch_fn(reinterpret_cast<const void *>(gv), wmax, kBlock, groups, p, stream)) != hipSuccess)
+        return e;
+    }
   }
-  // 4. reference gradients (fused inputs, when asked for)
-  if (fuse && p.grad_ref) {
+  // 4. reference gradients (fused inputs, when asked for) of workgroups that
+  //    did not hold whole queries
+  if (fuse && p.grad_ref && !p.ref_inblock) {
     const int64_t n = p.pairs / p.M * p.ref_dim;
     return launch_fn(reinterpret_cast<const void *>(ref_grad_kernel), (n + kBlock - 1) / kBlock, kBlock, 1, p, stream);
   }

@@ -156,7 +156,7 @@ def test_workspace_size_and_overlapping_levels():
     n = msda.msda_backward_workspace_size(COCO, STARTS, 2, 22223, 8, 32, 4, 22223, 4)
     samples = 2 * 22223 * 8 * 4 * 4
     pairs = 2 * 22223 * 8
-    assert 64 * samples + 24 * pairs <= n <= 64 * samples + 24 * pairs + (1 << 20)
+    assert 64 * samples + 16 * pairs <= n <= 64 * samples + 16 * pairs + (1 << 20)
     # overlapping level row ranges are rejected
     ss = np.array([[4, 4], [2, 2]], dtype=np.int64)
     ls = np.array([0, 14], dtype=np.int64)

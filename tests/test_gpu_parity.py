@@ -92,6 +92,19 @@ def test_bf16_backward_small_maps_full():
     assert_grad_loc(gl, rgl, w.spatial_shapes)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decoder_backward_full_config(dtype):
+    """Decoder-sized launch (few samples per value tile): grad_value comes from
+    per-sample atomics instead of the tile sort."""
+    w = config_workload("decoder_fwd_bf16", dtype=dtype, with_grad=True)
+    note(f"decoder backward full config N=2 Lq=300 COCO levels {dtype}")
+    gv, gl, ga = (to_f64(t) for t in gpu_backward(w))
+    rgv, rgl, rga = msda_backward(*_oracle_args(w), w.grad_out)
+    assert_f32("grad_value", gv, rgv)
+    assert_f32("grad_attn", ga, rga)
+    assert_grad_loc(gl, rgl, w.spatial_shapes)
+
+
 # ----------------------------------------------------- full-size configs, sampled outputs
 
 def test_encoder_forward_full_size_sampled():
