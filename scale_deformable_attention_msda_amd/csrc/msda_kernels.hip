@@ -133,17 +133,15 @@ __device__ __forceinline__ float dpp_mov(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
-// NaN-propagating maximum (a NaN operand gives NaN whichever side it is on).
-__device__ __forceinline__ float max_nan(float a, float b) { return (b > a || b != b) ? b : a; }
-
 // Sum (or maximum) over the `lpp` consecutive lanes of a pair; every lane
-// gets the result. Steps: quad xor 1, quad xor 2, mirror within 8, mirror
+// gets the result. (The maximum only keeps exp() in range for the softmax: a
+// NaN logit, which fmaxf skips, still turns its head's sum and weights NaN.) Steps: quad xor 1, quad xor 2, mirror within 8, mirror
 // within 16, then cross-row exchanges. Each step combines two disjoint
 // partial results, so the sum is identical in every lane of the group.
 template <int LPP, bool MAX = false>
 __device__ __forceinline__ float group_sum(float v, int lpp_rt) {
   const int lpp = LPP > 0 ? LPP : lpp_rt;
-  auto op = [](float a, float b) { return MAX ? max_nan(a, b) : a + b; };
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
   if (lpp >= 2) v = op(v, dpp_mov<0xB1>(v));   // quad_perm [1,0,3,2]
   if (lpp >= 4) v = op(v, dpp_mov<0x4E>(v));   // quad_perm [2,3,0,1]
   if (lpp >= 8) v = op(v, dpp_mov<0x141>(v));  // row_half_mirror
@@ -233,9 +231,10 @@ __device__ __forceinline__ Sample sample_geometry(const Params &p, uint32_t base
 
 __device__ __forceinline__ float softmax_weight(float z, float2 st) { return expf(z - st.x) * st.y; }
 
-// Reference point (x, y, 0, 0) or box (cx, cy, w, h) of the query of pair P.
-__device__ __forceinline__ float4 load_ref(const Params &p, uint32_t P) {
-  const float2 *r = reinterpret_cast<const float2 *>(p.ref + (size_t)(P / (uint32_t)p.M) * (size_t)p.ref_dim);
+// Reference point (x, y, 0, 0) or box (cx, cy, w, h) of query row q (image
+// and query flattened).
+__device__ __forceinline__ float4 load_ref(const Params &p, uint32_t q) {
+  const float2 *r = reinterpret_cast<const float2 *>(p.ref + (size_t)q * (size_t)p.ref_dim);
   const float2 c = r[0];
   if (p.ref_dim == 2) return make_float4(c.x, c.y, 0.0f, 0.0f);
   const float2 wh = r[1];
@@ -259,7 +258,7 @@ template <int LPP>
 __device__ __forceinline__ float2 pair_softmax_stats(const float *z, bool active, int j, int lpp, int LK) {
   float mx = -INFINITY;
   if (active)
-    for (int i = j; i < LK; i += lpp) mx = max_nan(mx, z[i]);
+    for (int i = j; i < LK; i += lpp) mx = fmaxf(mx, z[i]);
   mx = group_sum<LPP, true>(mx, lpp);
   float s = 0.0f;
   if (active)
@@ -288,7 +287,7 @@ template <typename T, int VEC, int NCG, int LPP, bool FUSE>
 __global__ __launch_bounds__(kBlock) void fwd_kernel(const Params p) {
   __shared__ FDesc desc[kDescCap];
   __shared__ uint32_t pbase[kBlock];
-  __shared__ float4 sref[FUSE ? kBlock : 1];  // reference of each pair's query
+  __shared__ uint32_t pqry[FUSE ? kBlock : 1];  // query row of each pair
   __shared__ float2 sst[FUSE ? kBlock : 1];   // softmax statistics of each pair
   __shared__ int32_t sH[kMaxLevels], sW[kMaxLevels], sS[kMaxLevels];
   load_levels(p, sH, sW, sS);
@@ -306,7 +305,7 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(const Params p) {
   const bool active = g < npairs;
   if (tid < npairs) pbase[tid] = pair_base(p, (uint32_t)(P0 + tid));
   if constexpr (FUSE) {
-    if (tid < npairs) sref[tid] = load_ref(p, (uint32_t)(P0 + tid));
+    if (tid < npairs) pqry[tid] = (uint32_t)(P0 + tid) / (uint32_t)p.M;
     if (!p.seg_softmax) {
       const float2 st = pair_softmax_stats<LPP>(p.attn + (active ? (P0 + g) * p.LK : 0), active, j, lpp, p.LK);
       if (active && j == 0) sst[g] = st;
@@ -344,7 +343,7 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(const Params p) {
       float2 xy = v;
       float A = z;
       if constexpr (FUSE) {
-        xy = form_loc<true>(p, v, l, sref[gg], sH, sW);
+        xy = form_loc<true>(p, v, l, load_ref(p, pqry[gg]), sH, sW);
         A = p.seg_softmax ? segment_softmax(z, p.LK) : softmax_weight(z, sst[gg]);
       }
       const Sample s = sample_geometry(p, pbase[gg], xy, A, l, sH, sW, sS);
@@ -413,9 +412,9 @@ struct __align__(16) BDesc {
 
 constexpr size_t kSampleSmemPlain =
     kDescCap * (sizeof(BDesc) + sizeof(float3) + 4) + 3 * kMaxLevels * 4 + kBlock * 4;
-// fused inputs add per pair: reference, softmax statistics, sum of A * grad_attn;
-// per staged sample: its offset
-constexpr size_t kSampleSmemFused = kSampleSmemPlain + kBlock * (16 + 8 + 4) + kDescCap * 8;
+// fused inputs add per pair: softmax statistics, sum of A * grad_attn, query
+// row; per staged sample: its offset
+constexpr size_t kSampleSmemFused = kSampleSmemPlain + kBlock * (8 + 4 + 4) + kDescCap * 8;
 template <bool FUSE>
 constexpr size_t sample_smem() { return FUSE ? kSampleSmemFused : kSampleSmemPlain; }
 
@@ -437,10 +436,10 @@ __device__ __forceinline__ void bwd_sample_body(const Params &p, int block, int 
   int32_t *sW = sH + kMaxLevels, *sS = sW + kMaxLevels;
   uint32_t *pbase = reinterpret_cast<uint32_t *>(sS + kMaxLevels);
   // fused inputs only
-  float4 *sref = reinterpret_cast<float4 *>(smem + kSampleSmemPlain);
-  float2 *sst = reinterpret_cast<float2 *>(sref + kBlock);
+  float2 *sst = reinterpret_cast<float2 *>(smem + kSampleSmemPlain);
   float2 *soff = reinterpret_cast<float2 *>(sst + kBlock);
   float *ssum = reinterpret_cast<float *>(soff + kDescCap);
+  uint32_t *pqry = reinterpret_cast<uint32_t *>(ssum + kBlock);
   float4 *sgr = reinterpret_cast<float4 *>(smem);  // reuses desc once the last chunk is done
   load_levels(p, sH, sW, sS);
 
@@ -455,7 +454,7 @@ __device__ __forceinline__ void bwd_sample_body(const Params &p, int block, int 
   const bool active = g < npairs;
   if (tid < npairs) pbase[tid] = pair_base(p, (uint32_t)(P0 + tid));
   if constexpr (FUSE) {
-    if (tid < npairs) sref[tid] = load_ref(p, (uint32_t)(P0 + tid));
+    if (tid < npairs) pqry[tid] = (uint32_t)(P0 + tid) / (uint32_t)p.M;
     if (!p.seg_softmax) {
       const float2 st = pair_softmax_stats<LPP>(p.attn + (active ? (P0 + g) * p.LK : 0), active, j, lpp, p.LK);
       if (active && j == 0) sst[g] = st;
@@ -494,7 +493,7 @@ __device__ __forceinline__ void bwd_sample_body(const Params &p, int block, int 
       float2 xy = v;
       float A = z;
       if constexpr (FUSE) {
-        xy = form_loc<true>(p, v, l, sref[gg], sH, sW);
+        xy = form_loc<true>(p, v, l, load_ref(p, pqry[gg]), sH, sW);
         A = p.seg_softmax ? segment_softmax(z, p.LK) : softmax_weight(z, sst[gg]);
         soff[pp * dstride + gg] = v;
       }
@@ -549,14 +548,24 @@ __device__ __forceinline__ void bwd_sample_body(const Params &p, int block, int 
         gx = group_sum<LPP>(gx, lpp);
         gy = group_sum<LPP>(gy, lpp);
         const float glx = d.aw * gx, gly = d.ah * gy;
-        if (j == 0) res[pp * dstride + g] = make_float3(ga, glx, gly);
+        float3 r = make_float3(ga, glx, gly);
+        if constexpr (FUSE) {
+          const float A = sA[pp * dstride + g];
+          // reference points: d loc / d offset = 1 / size cancels the size in
+          // grad_loc, so the offset gradient is A * d sample / d x itself (zero
+          // for a sample outside the map, as grad_loc is)
+          if (p.ref_dim == 2) r = make_float3(ga, d.aw != 0.0f ? A * gx : 0.0f, d.ah != 0.0f ? A * gy : 0.0f);
+        }
+        if (j == 0) res[pp * dstride + g] = r;
         if constexpr (FUSE) {
           acc_s = fmaf(sA[pp * dstride + g], ga, acc_s);
           acc_rx += glx;
           acc_ry += gly;
-          const float2 o = soff[pp * dstride + g];
-          acc_bx = fmaf(glx, o.x, acc_bx);
-          acc_by = fmaf(gly, o.y, acc_by);
+          if (p.ref_dim == 4) {
+            const float2 o = soff[pp * dstride + g];
+            acc_bx = fmaf(glx, o.x, acc_bx);
+            acc_by = fmaf(gly, o.y, acc_by);
+          }
         }
       }
       if constexpr (FUSE) {
@@ -575,11 +584,8 @@ __device__ __forceinline__ void bwd_sample_body(const Params &p, int block, int 
         // one chunk holds all of the pair's samples: its sum is complete here;
         // otherwise grad_attn is stored and finished below
         if (p.LK <= p.pc) gz = sA[pp * dstride + gg] * (r.x - ssum[gg]);
-        if (p.ref_dim == 2) {
-          const int l = (pc0 + pp) / p.K;
-          gl = make_float2(r.y / (float)sW[l], r.z / (float)sH[l]);
-        } else {
-          const float4 rf = sref[gg];
+        if (p.ref_dim == 4) {
+          const float4 rf = load_ref(p, pqry[gg]);
           gl = make_float2(r.y * rf.z, r.z * rf.w);
         }
       }
@@ -749,7 +755,7 @@ __global__ __launch_bounds__(kBlock) void bin_kernel(const Params p) {
     const int64_t sid = (int64_t)P * p.LK + pt;
     const int l = pt / p.K;
     float2 xy = *reinterpret_cast<const float2 *>(p.loc + 2 * sid);
-    if constexpr (FUSE) xy = form_loc<true>(p, xy, l, load_ref(p, P), sH, sW);
+    if constexpr (FUSE) xy = form_loc<true>(p, xy, l, load_ref(p, (uint32_t)(n * p.Lq + q0 + qi)), sH, sW);
     float A = 0.0f;
     if constexpr (MODE == 1) {
       A = p.attn[sid];
