@@ -6,4 +6,5 @@ code with the HIP path.
 """
 from .msda_oracle import (fused_locations, msda_backward, msda_forward,  # noqa: F401
                           msda_fused_backward, msda_fused_forward, msda_grad_value_rows,
-                          pixel_coordinate, softmax_weights)
+                          msda_grouped_backward, msda_grouped_forward, pixel_coordinate,
+                          softmax_weights)

@@ -363,3 +363,40 @@ def msda_fused_backward(value, spatial_shapes, level_start, ref, offsets, logits
         grad_ref = np.concatenate([gl.sum(axis=heads_levels_points),
                                    (gl * off).sum(axis=heads_levels_points)], axis=-1)
     return gv, grad_off, grad_logits, grad_ref
+
+
+# --- deformable groups ------------------------------------------------------------------------
+#
+# Page "Deformable Attention" (glossary), on heads and groups: heads are
+# gathered into fewer deformable groups that share one set of sampled keys
+# while keeping their own projections. Reading R12: G groups of M/G consecutive
+# heads; group g = m // (M/G) supplies the sampling locations and the weights of
+# head m; each head still reads its own value channels.
+
+def _heads_from_groups(a, M):
+    G = a.shape[2]
+    if M % G:
+        raise ValueError(f"groups ({G}) must divide heads ({M})")
+    return np.repeat(np.asarray(a), M // G, axis=2)
+
+
+def msda_grouped_forward(value, spatial_shapes, level_start, loc, attn, **kw):
+    """out[n,q,m,:] with loc [N,Lq,G,L,K,2] and attn [N,Lq,G,L,K] shared by the
+    M/G heads of each group: every head samples with its group's locations."""
+    M = np.asarray(value).shape[2]
+    return msda_forward(value, spatial_shapes, level_start, _heads_from_groups(loc, M),
+                        _heads_from_groups(attn, M), **kw)
+
+
+def msda_grouped_backward(value, spatial_shapes, level_start, loc, attn, grad_out, **kw):
+    """(grad_value, grad_loc [N,Lq,G,L,K,2], grad_attn [N,Lq,G,L,K]): a group's
+    location and weight feed all its heads, so their gradients are the sums of
+    the per-head gradients over the group's heads."""
+    M = np.asarray(value).shape[2]
+    G = np.asarray(loc).shape[2]
+    gv, gl, ga = msda_backward(value, spatial_shapes, level_start, _heads_from_groups(loc, M),
+                               _heads_from_groups(attn, M), grad_out, **kw)
+    N, Lq = gl.shape[:2]
+    gl = gl.reshape((N, Lq, G, M // G) + gl.shape[3:]).sum(axis=3)
+    ga = ga.reshape((N, Lq, G, M // G) + ga.shape[3:]).sum(axis=3)
+    return gv, gl, ga

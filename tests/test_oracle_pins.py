@@ -14,7 +14,8 @@ import numpy as np
 import pytest
 
 from oracle import (fused_locations, msda_backward, msda_forward, msda_fused_backward,
-                    msda_fused_forward, msda_grad_value_rows, pixel_coordinate, softmax_weights)
+                    msda_fused_forward, msda_grad_value_rows, msda_grouped_backward,
+                    msda_grouped_forward, pixel_coordinate, softmax_weights)
 from tests.dense_reference import (dense_forward_backward, exact_index_coordinate,
                                    round_fraction_to_f32)
 from workloads import init_pattern_workload, level_starts, uniform_workload
@@ -518,3 +519,66 @@ def test_fused_backward_query_subset_agrees_with_full(ref_dim):
     np.testing.assert_allclose(go_s, go[qn, qq], rtol=0, atol=1e-12)
     np.testing.assert_allclose(gz_s, gz[qn, qq], rtol=0, atol=1e-12)
     np.testing.assert_allclose(gr_s, gr[qn, qq], rtol=0, atol=1e-12)
+
+
+# --- deformable groups (reading R12) ---------------------------------------------------------
+
+def test_groups_of_one_head_are_the_core():
+    w = uniform_workload(N=1, shapes=((6, 7), (3, 4)), Lq=9, M=3, D=4, K=2, seed=120, with_grad=True)
+    args = (w.value, w.spatial_shapes, w.level_start, w.loc, w.attn)
+    np.testing.assert_array_equal(msda_grouped_forward(*args), msda_forward(*args))
+    for a, b in zip(msda_grouped_backward(*args, w.grad_out), msda_backward(*args, w.grad_out)):
+        np.testing.assert_array_equal(a, b)
+
+
+def test_grouped_heads_share_their_group_samples():
+    """With equal value channels in every head of a group, the heads of the group
+    return equal outputs; with the group's channels split across heads, the
+    heads' outputs add up to the core's output on the summed channels."""
+    rng = np.random.default_rng(121)
+    shapes = np.array([[5, 6], [3, 3]])
+    starts = np.array([0, 30])
+    N, Lq, M, G, D, L, K = 2, 7, 6, 2, 3, 2, 3
+    base = rng.standard_normal((N, 39, G, D))
+    value = np.repeat(base, M // G, axis=2)
+    loc = rng.uniform(-0.1, 1.1, (N, Lq, G, L, K, 2))
+    attn = rng.uniform(0, 1, (N, Lq, G, L, K))
+    out = msda_grouped_forward(value, shapes, starts, loc, attn).reshape(N, Lq, G, M // G, D)
+    for h in range(1, M // G):
+        np.testing.assert_allclose(out[:, :, :, h], out[:, :, :, 0], atol=1e-12)
+    np.testing.assert_allclose(out[:, :, :, 0], msda_forward(base, shapes, starts, loc, attn), atol=1e-12)
+    split = rng.standard_normal((N, 39, M, D))
+    tot = split.reshape(N, 39, G, M // G, D).sum(axis=3)
+    o2 = msda_grouped_forward(split, shapes, starts, loc, attn).reshape(N, Lq, G, M // G, D).sum(axis=3)
+    np.testing.assert_allclose(o2, msda_forward(tot, shapes, starts, loc, attn), atol=1e-12)
+
+
+def test_grouped_backward_finite_differences_and_adjoint():
+    rng = np.random.default_rng(122)
+    shapes = np.array([[6, 8], [3, 5]])
+    starts = np.array([0, 48])
+    N, Lq, M, G, D, L, K = 1, 4, 4, 2, 3, 2, 2
+    value = rng.standard_normal((N, 63, M, D))
+    loc = rng.uniform(0.05, 0.95, (N, Lq, G, L, K, 2))
+    attn = rng.uniform(0, 1, (N, Lq, G, L, K))
+    Gr = rng.standard_normal((N, Lq, M, D))
+    kw = dict(round_coords=False)
+    gv, gl, ga = msda_grouped_backward(value, shapes, starts, loc, attn, Gr, **kw)
+
+    def f(loc=loc, attn=attn):
+        return (msda_grouped_forward(value, shapes, starts, loc, attn, **kw) * Gr).sum()
+
+    h = 1e-6
+    for idx in [(0, 0, 0, 0, 0), (0, 3, 1, 1, 1), (0, 2, 1, 0, 1)]:
+        ap, am = attn.copy(), attn.copy()
+        ap[idx] += h
+        am[idx] -= h
+        assert abs((f(attn=ap) - f(attn=am)) / (2 * h) - ga[idx]) < 1e-6
+        for c in range(2):
+            lp, lm = loc.copy(), loc.copy()
+            lp[idx + (c,)] += h
+            lm[idx + (c,)] -= h
+            fd = (f(loc=lp) - f(loc=lm)) / (2 * h)
+            assert abs(fd - gl[idx + (c,)]) < 1e-4 * max(1.0, abs(fd)), (idx, c, fd, gl[idx + (c,)])
+    # out is linear in value: <G, out> = <grad_value, value>
+    assert abs(f() - (gv * value).sum()) < 1e-9 * max(1.0, abs(f()))
