@@ -197,6 +197,42 @@ msda_status msda_fused_backward(const void *value, const int64_t *spatial_shapes
                                 int64_t L, int64_t Lq, int64_t K, int dtype, void *workspace,
                                 size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Deformable groups (page "Deformable Attention", glossary: heads are gathered
+ * into fewer deformable groups that share one set of sampled keys while
+ * keeping their own projections). G groups of M/G consecutive heads: group
+ * g = m / (M/G) supplies the locations and weights of head m, and each head
+ * still reads its own value channels:
+ *   out[n,q,m,:] = sum_{l,k} attn[n,q,g,l,k] *
+ *                  bilinear(value[n, level l, m, :], loc[n,q,g,l,k,:])
+ * Layouts: loc [N, Lq, G, L, K, 2], attn [N, Lq, G, L, K]; value, out,
+ * grad_out and grad_value as for msda_forward (M heads of D channels).
+ * grad_loc [N, Lq, G, L, K, 2] and grad_attn [N, Lq, G, L, K] sum the
+ * per-head gradients over the heads of each group. G must divide M
+ * (MSDA_ERROR_INVALID_VALUE otherwise) and (M/G)*D must be within
+ * MSDA_MAX_CHANNELS. The heads of a group are consecutive channels of a value
+ * or out row, so these calls run the sampling core with G heads of (M/G)*D
+ * channels; msda_fused_forward / msda_fused_backward take groups the same way
+ * (pass M = G and D = (M/G)*D). Everything else as for msda_forward,
+ * msda_backward_workspace_size and msda_backward.
+ */
+msda_status msda_grouped_forward(const void *value, const int64_t *spatial_shapes,
+                                 const int64_t *level_start, const float *loc, const float *attn,
+                                 void *out, int64_t N, int64_t S, int64_t M, int64_t D, int64_t L,
+                                 int64_t Lq, int64_t K, int64_t G, int dtype, hipStream_t stream);
+
+msda_status msda_grouped_backward_workspace_size(const int64_t *spatial_shapes,
+                                                 const int64_t *level_start, int64_t N, int64_t S,
+                                                 int64_t M, int64_t D, int64_t L, int64_t Lq,
+                                                 int64_t K, int64_t G, int dtype, size_t *bytes);
+
+msda_status msda_grouped_backward(const void *value, const int64_t *spatial_shapes,
+                                  const int64_t *level_start, const float *loc, const float *attn,
+                                  const void *grad_out, float *grad_value, float *grad_loc,
+                                  float *grad_attn, int64_t N, int64_t S, int64_t M, int64_t D,
+                                  int64_t L, int64_t Lq, int64_t K, int64_t G, int dtype,
+                                  void *workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Static description of a status code; never NULL. */
 const char *msda_status_string(msda_status status);
 

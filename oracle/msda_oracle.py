@@ -315,9 +315,11 @@ def _round_sum_to_f32(a, b):
 
 def msda_fused_forward(value, spatial_shapes, level_start, ref, offsets, logits, **kw):
     """out from the raw step before the core: locations from (ref, offsets),
-    weights = softmax(logits); then the sampling core."""
+    weights = softmax(logits); then the sampling core (with deformable groups
+    when offsets has fewer heads than value, reading R12)."""
     loc = fused_locations(ref, offsets, spatial_shapes, exact=kw.pop("exact_locations", False))
-    return msda_forward(value, spatial_shapes, level_start, loc, softmax_weights(logits), **kw)
+    core = msda_forward if np.shape(offsets)[2] == np.shape(value)[2] else msda_grouped_forward
+    return core(value, spatial_shapes, level_start, loc, softmax_weights(logits), **kw)
 
 
 def msda_fused_backward(value, spatial_shapes, level_start, ref, offsets, logits, grad_out, queries=None,
@@ -337,7 +339,8 @@ def msda_fused_backward(value, spatial_shapes, level_start, ref, offsets, logits
     off = np.asarray(offsets, dtype=np.float64)
     ref64 = np.asarray(ref, dtype=np.float64)
     if queries is None:
-        gv, gl, ga = msda_backward(value, spatial_shapes, level_start, loc, A, grad_out, **kw)
+        core = msda_backward if off.shape[2] == np.shape(value)[2] else msda_grouped_backward
+        gv, gl, ga = core(value, spatial_shapes, level_start, loc, A, grad_out, **kw)
     else:
         qn, qq = (np.asarray(a, dtype=np.int64) for a in queries)
         Q, M = len(qn), off.shape[2]

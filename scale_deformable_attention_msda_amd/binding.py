@@ -56,6 +56,12 @@ def load_library():
     lib.msda_fused_forward.restype = ci
     lib.msda_fused_backward.argtypes = [vp] * 4 + [ci] + [vp] * 7 + [i64] * 7 + [ci, vp, ctypes.c_size_t, vp]
     lib.msda_fused_backward.restype = ci
+    lib.msda_grouped_forward.argtypes = [vp] * 6 + [i64] * 8 + [ci, vp]
+    lib.msda_grouped_forward.restype = ci
+    lib.msda_grouped_backward.argtypes = [vp] * 9 + [i64] * 8 + [ci, vp, ctypes.c_size_t, vp]
+    lib.msda_grouped_backward.restype = ci
+    lib.msda_grouped_backward_workspace_size.argtypes = [vp, vp] + [i64] * 8 + [ci, ctypes.POINTER(ctypes.c_size_t)]
+    lib.msda_grouped_backward_workspace_size.restype = ci
     lib.msda_status_string.argtypes = [ci]
     lib.msda_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -90,15 +96,19 @@ def _dtype_code(t):
     raise ValueError(f"unsupported dtype {t}: float32 or bfloat16")
 
 
-def _dims(value, loc, attn):
+def _dims(value, loc, attn, grouped=False):
     if value.dim() != 4 or loc.dim() != 6 or attn.dim() != 5:
         raise ValueError("expected value [N,S,M,D], loc [N,Lq,M,L,K,2], attn [N,Lq,M,L,K]")
     N, S, M, D = value.shape
     N2, Lq, M2, L, K, two = loc.shape
-    if (N2, M2, two) != (N, M, 2) or tuple(attn.shape) != (N, Lq, M, L, K):
+    if grouped:
+        ok = M2 >= 1 and M % M2 == 0
+    else:
+        ok = M2 == M
+    if (N2, two) != (N, 2) or not ok or tuple(attn.shape) != (N, Lq, M2, L, K):
         raise ValueError(f"shape mismatch: value {tuple(value.shape)}, loc {tuple(loc.shape)}, "
                          f"attn {tuple(attn.shape)}")
-    return N, S, M, D, L, Lq, K
+    return (N, S, M, D, L, Lq, K, M2) if grouped else (N, S, M, D, L, Lq, K)
 
 
 def _device_tensor(t, what, dtype=None):
@@ -199,16 +209,19 @@ def msda_backward(value, spatial_shapes, level_start, loc, attn, grad_out, grad_
 
 
 def _fused_dims(value, ref, offsets, logits):
+    """Sizes for the fused entry points. offsets / logits may carry G < M
+    deformable groups (G dividing M); the call then runs with G heads of
+    (M/G)*D channels, which is the same memory layout of value and out."""
     if value.dim() != 4 or ref.dim() != 3 or offsets.dim() != 6 or logits.dim() != 5:
-        raise ValueError("expected value [N,S,M,D], ref [N,Lq,2|4], offsets [N,Lq,M,L,K,2], "
-                         "logits [N,Lq,M,L,K]")
+        raise ValueError("expected value [N,S,M,D], ref [N,Lq,2|4], offsets [N,Lq,G,L,K,2], "
+                         "logits [N,Lq,G,L,K]")
     N, S, M, D = value.shape
-    N2, Lq, M2, L, K, two = offsets.shape
-    if (N2, M2, two) != (N, M, 2) or tuple(logits.shape) != (N, Lq, M, L, K) or \
+    N2, Lq, G, L, K, two = offsets.shape
+    if (N2, two) != (N, 2) or G < 1 or M % G != 0 or tuple(logits.shape) != (N, Lq, G, L, K) or \
             tuple(ref.shape[:2]) != (N, Lq) or ref.shape[2] not in (2, 4):
         raise ValueError(f"shape mismatch: value {tuple(value.shape)}, ref {tuple(ref.shape)}, "
                          f"offsets {tuple(offsets.shape)}, logits {tuple(logits.shape)}")
-    return N, S, M, D, L, Lq, K, int(ref.shape[2])
+    return N, S, M, D, L, Lq, K, int(ref.shape[2]), G
 
 
 def msda_fused_forward(value, spatial_shapes, level_start, ref, offsets, logits, out=None, stream=None):
@@ -220,7 +233,7 @@ def msda_fused_forward(value, spatial_shapes, level_start, ref, offsets, logits,
     dt = _dtype_code(value.dtype)
     for t, name in ((ref, "ref"), (offsets, "offsets"), (logits, "logits")):
         _device_tensor(t, name, torch.float32)
-    N, S, M, D, L, Lq, K, rd = _fused_dims(value, ref, offsets, logits)
+    N, S, M, D, L, Lq, K, rd, G = _fused_dims(value, ref, offsets, logits)
     ss = _host_i64(spatial_shapes, (L, 2), "spatial_shapes")
     ls = _host_i64(level_start, (L,), "level_start")
     if out is None:
@@ -232,8 +245,8 @@ def msda_fused_forward(value, spatial_shapes, level_start, ref, offsets, logits,
     with torch.cuda.device(value.device):
         s = torch.cuda.current_stream().cuda_stream if stream is None else int(stream)
         _raise(lib.msda_fused_forward(value.data_ptr(), ss.ctypes.data, ls.ctypes.data, ref.data_ptr(), rd,
-                                      offsets.data_ptr(), logits.data_ptr(), out.data_ptr(), N, S, M, D, L,
-                                      Lq, K, dt, s))
+                                      offsets.data_ptr(), logits.data_ptr(), out.data_ptr(), N, S, G,
+                                      M // G * D, L, Lq, K, dt, s))
     return out
 
 
@@ -248,7 +261,7 @@ def msda_fused_backward(value, spatial_shapes, level_start, ref, offsets, logits
     for t, name in ((ref, "ref"), (offsets, "offsets"), (logits, "logits")):
         _device_tensor(t, name, torch.float32)
     _device_tensor(grad_out, "grad_out", value.dtype)
-    N, S, M, D, L, Lq, K, rd = _fused_dims(value, ref, offsets, logits)
+    N, S, M, D, L, Lq, K, rd, G = _fused_dims(value, ref, offsets, logits)
     if tuple(grad_out.shape) != (N, Lq, M, D):
         raise ValueError(f"grad_out must be {(N, Lq, M, D)}")
     ss = _host_i64(spatial_shapes, (L, 2), "spatial_shapes")
@@ -257,20 +270,20 @@ def msda_fused_backward(value, spatial_shapes, level_start, ref, offsets, logits
     if grad_value is None:
         grad_value = torch.empty((N, S, M, D), dtype=torch.float32, device=dev)
     if grad_offsets is None:
-        grad_offsets = torch.empty((N, Lq, M, L, K, 2), dtype=torch.float32, device=dev)
+        grad_offsets = torch.empty((N, Lq, G, L, K, 2), dtype=torch.float32, device=dev)
     if grad_logits is None:
-        grad_logits = torch.empty((N, Lq, M, L, K), dtype=torch.float32, device=dev)
+        grad_logits = torch.empty((N, Lq, G, L, K), dtype=torch.float32, device=dev)
     if grad_ref is None and need_grad_ref:
         grad_ref = torch.empty((N, Lq, rd), dtype=torch.float32, device=dev)
-    outs = [(grad_value, "grad_value", (N, S, M, D)), (grad_offsets, "grad_offsets", (N, Lq, M, L, K, 2)),
-            (grad_logits, "grad_logits", (N, Lq, M, L, K))]
+    outs = [(grad_value, "grad_value", (N, S, M, D)), (grad_offsets, "grad_offsets", (N, Lq, G, L, K, 2)),
+            (grad_logits, "grad_logits", (N, Lq, G, L, K))]
     if grad_ref is not None:
         outs.append((grad_ref, "grad_ref", (N, Lq, rd)))
     for t, name, shape in outs:
         _device_tensor(t, name, torch.float32)
         if tuple(t.shape) != shape:
             raise ValueError(f"{name} must be {shape}")
-    need = msda_backward_workspace_size(ss, ls, N, S, M, D, L, Lq, K, dt)
+    need = msda_backward_workspace_size(ss, ls, N, S, G, M // G * D, L, Lq, K, dt)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     else:
@@ -281,8 +294,77 @@ def msda_fused_backward(value, spatial_shapes, level_start, ref, offsets, logits
                                        offsets.data_ptr(), logits.data_ptr(), grad_out.data_ptr(),
                                        grad_value.data_ptr(), grad_offsets.data_ptr(), grad_logits.data_ptr(),
                                        grad_ref.data_ptr() if grad_ref is not None else None,
-                                       N, S, M, D, L, Lq, K, dt, workspace.data_ptr(), workspace.numel(), s))
+                                       N, S, G, M // G * D, L, Lq, K, dt, workspace.data_ptr(), workspace.numel(),
+                                       s))
     return grad_value, grad_offsets, grad_logits, grad_ref
+
+
+def msda_grouped_forward(value, spatial_shapes, level_start, loc, attn, out=None, stream=None):
+    """out[N,Lq,M,D] with deformable groups: loc [N,Lq,G,L,K,2] and attn
+    [N,Lq,G,L,K] shared by the M/G consecutive heads of each group."""
+    lib = load_library()
+    _device_tensor(value, "value")
+    dt = _dtype_code(value.dtype)
+    _device_tensor(loc, "loc", torch.float32)
+    _device_tensor(attn, "attn", torch.float32)
+    N, S, M, D, L, Lq, K, G = _dims(value, loc, attn, grouped=True)
+    ss = _host_i64(spatial_shapes, (L, 2), "spatial_shapes")
+    ls = _host_i64(level_start, (L,), "level_start")
+    if out is None:
+        out = torch.empty((N, Lq, M, D), dtype=value.dtype, device=value.device)
+    else:
+        _device_tensor(out, "out", value.dtype)
+        if tuple(out.shape) != (N, Lq, M, D):
+            raise ValueError(f"out must be {(N, Lq, M, D)}")
+    with torch.cuda.device(value.device):
+        s = torch.cuda.current_stream().cuda_stream if stream is None else int(stream)
+        _raise(lib.msda_grouped_forward(value.data_ptr(), ss.ctypes.data, ls.ctypes.data, loc.data_ptr(),
+                                        attn.data_ptr(), out.data_ptr(), N, S, M, D, L, Lq, K, G, dt, s))
+    return out
+
+
+def msda_grouped_backward(value, spatial_shapes, level_start, loc, attn, grad_out, grad_value=None,
+                          grad_loc=None, grad_attn=None, workspace=None, stream=None):
+    """(grad_value [N,S,M,D], grad_loc [N,Lq,G,L,K,2], grad_attn [N,Lq,G,L,K]) of
+    msda_grouped_forward, float32."""
+    lib = load_library()
+    _device_tensor(value, "value")
+    dt = _dtype_code(value.dtype)
+    _device_tensor(loc, "loc", torch.float32)
+    _device_tensor(attn, "attn", torch.float32)
+    _device_tensor(grad_out, "grad_out", value.dtype)
+    N, S, M, D, L, Lq, K, G = _dims(value, loc, attn, grouped=True)
+    if tuple(grad_out.shape) != (N, Lq, M, D):
+        raise ValueError(f"grad_out must be {(N, Lq, M, D)}")
+    ss = _host_i64(spatial_shapes, (L, 2), "spatial_shapes")
+    ls = _host_i64(level_start, (L,), "level_start")
+    dev = value.device
+    if grad_value is None:
+        grad_value = torch.empty((N, S, M, D), dtype=torch.float32, device=dev)
+    if grad_loc is None:
+        grad_loc = torch.empty((N, Lq, G, L, K, 2), dtype=torch.float32, device=dev)
+    if grad_attn is None:
+        grad_attn = torch.empty((N, Lq, G, L, K), dtype=torch.float32, device=dev)
+    for t, name, shape in ((grad_value, "grad_value", (N, S, M, D)),
+                           (grad_loc, "grad_loc", (N, Lq, G, L, K, 2)),
+                           (grad_attn, "grad_attn", (N, Lq, G, L, K))):
+        _device_tensor(t, name, torch.float32)
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be {shape}")
+    need = ctypes.c_size_t(0)
+    _raise(lib.msda_grouped_backward_workspace_size(ss.ctypes.data, ls.ctypes.data, N, S, M, D, L, Lq, K, G, dt,
+                                                    ctypes.byref(need)))
+    if workspace is None:
+        workspace = torch.empty(max(need.value, 1), dtype=torch.uint8, device=dev)
+    else:
+        _device_tensor(workspace, "workspace", torch.uint8)
+    with torch.cuda.device(dev):
+        s = torch.cuda.current_stream().cuda_stream if stream is None else int(stream)
+        _raise(lib.msda_grouped_backward(value.data_ptr(), ss.ctypes.data, ls.ctypes.data, loc.data_ptr(),
+                                         attn.data_ptr(), grad_out.data_ptr(), grad_value.data_ptr(),
+                                         grad_loc.data_ptr(), grad_attn.data_ptr(), N, S, M, D, L, Lq, K, G,
+                                         dt, workspace.data_ptr(), workspace.numel(), s))
+    return grad_value, grad_loc, grad_attn
 
 
 class MSDeformAttnSampling(torch.autograd.Function):

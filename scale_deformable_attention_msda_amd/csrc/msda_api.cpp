@@ -238,6 +238,43 @@ msda_status msda_fused_backward(const void *value, const int64_t *spatial_shapes
                        workspace_bytes, stream);
 }
 
+// Deformable groups: the M/G heads of a group are consecutive channels of a
+// value row and of an out row, so grouped sampling is the sampling core with G
+// heads of (M/G)*D channels each.
+static bool group_shape(int64_t M, int64_t D, int64_t G, int64_t *Dg) {
+  if (G < 1 || M < 1 || M % G != 0) return false;
+  return mul_ok(M / G, D, Dg);
+}
+
+msda_status msda_grouped_forward(const void *value, const int64_t *spatial_shapes, const int64_t *level_start,
+                                 const float *loc, const float *attn, void *out, int64_t N, int64_t S, int64_t M,
+                                 int64_t D, int64_t L, int64_t Lq, int64_t K, int64_t G, int dtype,
+                                 hipStream_t stream) {
+  int64_t Dg;
+  if (!group_shape(M, D, G, &Dg)) return MSDA_ERROR_INVALID_VALUE;
+  return forward_impl(value, spatial_shapes, level_start, loc, attn, nullptr, 0, out, N, S, G, Dg, L, Lq, K, dtype,
+                      stream);
+}
+
+msda_status msda_grouped_backward_workspace_size(const int64_t *spatial_shapes, const int64_t *level_start,
+                                                 int64_t N, int64_t S, int64_t M, int64_t D, int64_t L, int64_t Lq,
+                                                 int64_t K, int64_t G, int dtype, size_t *bytes) {
+  int64_t Dg;
+  if (!group_shape(M, D, G, &Dg)) return MSDA_ERROR_INVALID_VALUE;
+  return msda_backward_workspace_size(spatial_shapes, level_start, N, S, G, Dg, L, Lq, K, dtype, bytes);
+}
+
+msda_status msda_grouped_backward(const void *value, const int64_t *spatial_shapes, const int64_t *level_start,
+                                  const float *loc, const float *attn, const void *grad_out, float *grad_value,
+                                  float *grad_loc, float *grad_attn, int64_t N, int64_t S, int64_t M, int64_t D,
+                                  int64_t L, int64_t Lq, int64_t K, int64_t G, int dtype, void *workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  int64_t Dg;
+  if (!group_shape(M, D, G, &Dg)) return MSDA_ERROR_INVALID_VALUE;
+  return backward_impl(value, spatial_shapes, level_start, loc, attn, nullptr, 0, grad_out, grad_value, grad_loc,
+                       grad_attn, nullptr, N, S, G, Dg, L, Lq, K, dtype, workspace, workspace_bytes, stream);
+}
+
 const char *msda_status_string(msda_status status) {
   switch (status) {
     case MSDA_SUCCESS: return "MSDA_SUCCESS: no error";

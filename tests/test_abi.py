@@ -28,8 +28,9 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["msda_backward", "msda_backward_workspace_size", "msda_forward",
-                                    "msda_fused_backward", "msda_fused_forward", "msda_status_string",
-                                    "msda_validate"]
+                                    "msda_fused_backward", "msda_fused_forward", "msda_grouped_backward",
+                                    "msda_grouped_backward_workspace_size", "msda_grouped_forward",
+                                    "msda_status_string", "msda_validate"]
 
 
 def test_library_exports_every_declared_symbol():
@@ -149,6 +150,27 @@ def test_fused_entry_points_reject_bad_arguments_before_any_hip_call():
     # empty problems are no-ops
     assert lib.msda_fused_forward(None, ss, ls, None, 2, None, None, None, 0, 22223, 8, 32, 4, 10, 4, 0,
                                   None) == 0
+
+
+def test_grouped_entry_points_check_groups():
+    lib = binding.load_library()
+    ss = COCO.ctypes.data
+    ls = STARTS.ctypes.data
+    A, W, WB = 0x10000, 0x100000, 1 << 40
+    # G must divide M
+    for G in (0, -1, 3, 16):
+        dims = (1, 22223, 8, 32, 4, 22223, 4, G)
+        assert lib.msda_grouped_forward(A, ss, ls, A, A, A, *dims, 0, None) == 1
+        assert lib.msda_grouped_backward(A, ss, ls, A, A, A, A, A, A, *dims, 0, W, WB, None) == 1
+    # (M/G)*D beyond the channel limit: 8 heads of 256 channels in one group
+    assert lib.msda_grouped_forward(A, ss, ls, A, A, A, 1, 22223, 8, 256, 4, 22223, 4, 1, 0, None) == 2
+    # a group's workspace is the core's with G heads of (M/G)*D channels
+    n_g = ctypes.c_size_t(0)
+    assert lib.msda_grouped_backward_workspace_size(ss, ls, 1, 22223, 8, 32, 4, 22223, 4, 2, 0,
+                                                    ctypes.byref(n_g)) == 0
+    assert n_g.value == msda.msda_backward_workspace_size(COCO, STARTS, 1, 22223, 2, 128, 4, 22223, 4)
+    # misalignment is checked on the group shape: 128 bf16 channels, value 2 bytes off
+    assert lib.msda_grouped_forward(A + 1, ss, ls, A, A, A, 1, 22223, 8, 32, 4, 22223, 4, 2, 1, None) == 3
 
 
 def test_workspace_size_and_overlapping_levels():

@@ -90,8 +90,8 @@ class Workload:
     @property
     def dims(self):
         N, S, M, D = self.value.shape
-        _, Lq, _, L, K, _ = self.loc.shape
-        return dict(N=N, S=S, M=M, D=D, L=L, Lq=Lq, K=K)
+        _, Lq, G, L, K, _ = self.loc.shape
+        return dict(N=N, S=S, M=M, D=D, L=L, Lq=Lq, K=K, G=G)
 
     @property
     def points(self):
@@ -136,11 +136,13 @@ def _attn(rng, N, Lq, M, L, K):
 
 
 def encoder_workload(N=1, shapes=COCO_LEVELS, M=8, D=32, K=4, dtype="f32", seed=2,
-                     offset_px=2.0, with_grad=False, name="encoder"):
+                     offset_px=2.0, with_grad=False, name="encoder", groups=None):
     """Encoder-style input: every pixel of every level is a query (Lq = S, query
     q is flattened pixel q), its reference point is its pixel centre, and point k
     of head m at level l sits at that reference plus a N(0, offset_px) pixel
-    offset per axis in level-l pixels."""
+    offset per axis in level-l pixels. ``groups``: loc and attn carry that many
+    deformable groups instead of M heads."""
+    H = M if groups is None else groups
     shapes = tuple(tuple(int(v) for v in hw) for hw in shapes)
     L = len(shapes)
     starts, S = level_starts(shapes)
@@ -154,9 +156,9 @@ def encoder_workload(N=1, shapes=COCO_LEVELS, M=8, D=32, K=4, dtype="f32", seed=
         ref[s0:s0 + h * w, 0] = ((xx + 0.5) / w).ravel()
         ref[s0:s0 + h * w, 1] = ((yy + 0.5) / h).ravel()
     wh = np.asarray([[w, h] for h, w in shapes], dtype=np.float64)  # [L,2] as (W,H)
-    off = rng.standard_normal((N, Lq, M, L, K, 2)) * offset_px
+    off = rng.standard_normal((N, Lq, H, L, K, 2)) * offset_px
     loc = (ref[None, :, None, None, None, :] + off / wh[None, None, None, :, None, :]).astype(np.float32)
-    attn = _attn(rng, N, Lq, M, L, K)
+    attn = _attn(rng, N, Lq, H, L, K)
     g, g_bits = _grad_out(rng, (N, Lq, M, D), dtype) if with_grad else (None, None)
     return Workload(name, dtype, value, np.asarray(shapes, dtype=np.int64), starts, loc, attn,
                     g, value_bits, g_bits,
@@ -164,9 +166,11 @@ def encoder_workload(N=1, shapes=COCO_LEVELS, M=8, D=32, K=4, dtype="f32", seed=
 
 
 def decoder_workload(N=2, shapes=COCO_LEVELS, Lq=300, M=8, D=32, K=4, dtype="bf16", seed=3,
-                     offset_px=4.0, with_grad=False, name="decoder"):
+                     offset_px=4.0, with_grad=False, name="decoder", groups=None):
     """Decoder-style input: Lq object queries per image with reference points
-    uniform in [0,1]^2, plus N(0, offset_px) pixel offsets per level."""
+    uniform in [0,1]^2, plus N(0, offset_px) pixel offsets per level.
+    ``groups``: loc and attn carry that many deformable groups instead of M heads."""
+    H = M if groups is None else groups
     shapes = tuple(tuple(int(v) for v in hw) for hw in shapes)
     L = len(shapes)
     starts, S = level_starts(shapes)
@@ -174,9 +178,9 @@ def decoder_workload(N=2, shapes=COCO_LEVELS, Lq=300, M=8, D=32, K=4, dtype="bf1
     value, value_bits = _value(rng, (N, S, M, D), "normal", dtype)
     ref = rng.uniform(0.0, 1.0, (N, Lq, 2))
     wh = np.asarray([[w, h] for h, w in shapes], dtype=np.float64)
-    off = rng.standard_normal((N, Lq, M, L, K, 2)) * offset_px
+    off = rng.standard_normal((N, Lq, H, L, K, 2)) * offset_px
     loc = (ref[:, :, None, None, None, :] + off / wh[None, None, None, :, None, :]).astype(np.float32)
-    attn = _attn(rng, N, Lq, M, L, K)
+    attn = _attn(rng, N, Lq, H, L, K)
     g, g_bits = _grad_out(rng, (N, Lq, M, D), dtype) if with_grad else (None, None)
     return Workload(name, dtype, value, np.asarray(shapes, dtype=np.int64), starts, loc, attn,
                     g, value_bits, g_bits,
@@ -223,8 +227,8 @@ class FusedWorkload:
     @property
     def dims(self):
         N, S, M, D = self.value.shape
-        _, Lq, _, L, K, _ = self.offsets.shape
-        return dict(N=N, S=S, M=M, D=D, L=L, Lq=Lq, K=K, ref_dim=self.ref.shape[-1])
+        _, Lq, G, L, K, _ = self.offsets.shape
+        return dict(N=N, S=S, M=M, D=D, L=L, Lq=Lq, K=K, G=G, ref_dim=self.ref.shape[-1])
 
     @property
     def points(self):
@@ -233,7 +237,7 @@ class FusedWorkload:
 
 
 def fused_workload(kind="encoder", N=1, shapes=COCO_LEVELS, Lq=300, M=8, D=32, K=4, dtype="f32", seed=8,
-                   ref_dim=2, offset_px=2.0, box_offset_sd=0.25, with_grad=False, name=None):
+                   ref_dim=2, offset_px=2.0, box_offset_sd=0.25, with_grad=False, name=None, groups=None):
     """Raw inputs of the step before the sampling core.
 
     kind "encoder": every pixel is a query (Lq = S) with its pixel centre as
@@ -265,8 +269,9 @@ def fused_workload(kind="encoder", N=1, shapes=COCO_LEVELS, Lq=300, M=8, D=32, K
     else:
         raise ValueError(ref_dim)
     sd = offset_px if ref_dim == 2 else box_offset_sd
-    offsets = (rng.standard_normal((N, Lq, M, L, K, 2)) * sd).astype(np.float32)
-    logits = rng.standard_normal((N, Lq, M, L, K)).astype(np.float32)
+    H = M if groups is None else groups  # deformable groups, when given
+    offsets = (rng.standard_normal((N, Lq, H, L, K, 2)) * sd).astype(np.float32)
+    logits = rng.standard_normal((N, Lq, H, L, K)).astype(np.float32)
     g, g_bits = _grad_out(rng, (N, Lq, M, D), dtype) if with_grad else (None, None)
     return FusedWorkload(name or f"fused_{kind}_ref{ref_dim}", dtype, value, np.asarray(shapes, dtype=np.int64),
                          starts, np.ascontiguousarray(ref, dtype=np.float32), offsets, logits, g, value_bits,
