@@ -199,6 +199,56 @@ def fused_passes(msda, torch, dev, steps, rotate):
     return res
 
 
+def grouped_passes(msda, torch, dev, steps, rotate, groups=(1, 2, 4)):
+    """The encoder shape with G deformable groups (loc and attn shared by the
+    M/G heads of a group): forward and backward per pass, per G."""
+    import numpy as np
+
+    from workloads import encoder_workload
+
+    res = {"workload": "encoder shape as above, loc/attn per deformable group"}
+    stream = torch.cuda.current_stream()
+    for G in groups:
+        w = encoder_workload(N=1, M=8, D=32, K=4, seed=2, groups=G, with_grad=True)
+        d = w.dims
+        ss, ls = w.spatial_shapes, w.level_start
+        sets = []
+        for _ in range(rotate):
+            s = {"value": torch.from_numpy(w.value).to(dev), "loc": torch.from_numpy(w.loc).to(dev),
+                 "attn": torch.from_numpy(w.attn).to(dev), "g": torch.from_numpy(w.grad_out).to(dev)}
+            s["out"] = torch.empty((d["N"], d["Lq"], d["M"], d["D"]), dtype=torch.float32, device=dev)
+            s["gv"] = torch.empty_like(s["value"])
+            s["gl"] = torch.empty_like(s["loc"])
+            s["ga"] = torch.empty_like(s["attn"])
+            sets.append(s)
+
+        def fwd(s):
+            msda.msda_grouped_forward(s["value"], ss, ls, s["loc"], s["attn"], out=s["out"])
+
+        def bwd(s):
+            msda.msda_grouped_backward(s["value"], ss, ls, s["loc"], s["attn"], s["g"], grad_value=s["gv"],
+                                       grad_loc=s["gl"], grad_attn=s["ga"])
+
+        entry = {}
+        for name, fn in (("fwd", fwd), ("bwd", bwd)):
+            for i in range(3):
+                fn(sets[i % rotate])
+            torch.cuda.synchronize()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(steps)]
+            for i in range(steps):
+                ev[i][0].record(stream)
+                fn(sets[i % rotate])
+                ev[i][1].record(stream)
+            torch.cuda.synchronize()
+            ms = np.array([a.elapsed_time(b) for a, b in ev])
+            entry[name + "_us_mean"] = round(float(ms.mean()) * 1e3, 2)
+        entry["points_per_s_fwd_bwd"] = w.points / ((entry["fwd_us_mean"] + entry["bwd_us_mean"]) * 1e-6)
+        res[f"G={G}"] = entry
+        del sets
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -324,6 +374,7 @@ def main():
     }
     result["decoder_latency"] = decoder_latency(msda, torch, dev)
     result["fused_inputs"] = fused_passes(msda, torch, dev, min(args.steps, 30), args.rotate)
+    result["deformable_groups"] = grouped_passes(msda, torch, dev, min(args.steps, 20), args.rotate)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
     print(json.dumps(result), flush=True)

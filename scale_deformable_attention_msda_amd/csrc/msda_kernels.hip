@@ -1001,6 +1001,11 @@ __device__ __forceinline__ void gv_body(const Params &p, uint32_t bx, int cgroup
   const int cbeg = c0 + slice * Cs;               // first channel of this thread
   const int cnum = max(0, min(Cs, Dc - slice * Cs));  // channels it owns
   const bool vec = p.gvec != 0 && Cs == CS && (Cs % VG) == 0;
+  // Channel of this thread's accumulator c. With 16-byte loads the four
+  // threads of a pixel take interleaved 16-byte pieces of the row, so each
+  // load instruction reads whole 64-byte segments; otherwise each thread owns
+  // a contiguous run of Cs channels.
+  auto chan = [&](int c) { return vec ? c0 + (c / VG) * 4 * VG + slice * VG + (c % VG) : cbeg + c; };
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.grad_out, (uint32_t)(p.pairs * p.D) * (uint32_t)T::size);
   float acc[CS];
 #pragma unroll
@@ -1019,9 +1024,10 @@ __device__ __forceinline__ void gv_body(const Params &p, uint32_t bx, int cgroup
       const uint32_t base = ok ? r2.x * (uint32_t)p.D + (uint32_t)cbeg : kOobElem;
       if constexpr (CS >= VG) {
         if (vec) {
+          const uint32_t vbase = ok ? r2.x * (uint32_t)p.D + (uint32_t)(c0 + slice * VG) : kOobElem;
 #pragma unroll
           for (int q = 0; q < CS / VG; ++q)
-            load_vals<T, VG>(ro, (base + (uint32_t)(q * VG)) * (uint32_t)T::size,
+            load_vals<T, VG>(ro, (vbase + (uint32_t)(q * 4 * VG)) * (uint32_t)T::size,
                              *reinterpret_cast<float(*)[VG]>(&g[u][q * VG]));
           continue;
         }
@@ -1046,7 +1052,7 @@ __device__ __forceinline__ void gv_body(const Params &p, uint32_t bx, int cgroup
     const int DcP = Cs * 4;
 #pragma unroll
     for (int c = 0; c < CS; ++c)
-      if (c < Cs) stage[pix * DcP + slice * Cs + c] = acc[c];
+      if (c < Cs) stage[pix * DcP + chan(c) - c0] = acc[c];
     __syncthreads();
     for (int i = tid; i < kTilePix * Dc; i += kBlock) {
       const int q = i / Dc, c = i - q * Dc;
@@ -1058,10 +1064,17 @@ __device__ __forceinline__ void gv_body(const Params &p, uint32_t bx, int cgroup
   }
   const int py = ty * kTile + (pix >> 3), px = tx * kTile + (pix & 7);
   if (py >= H || px >= W) return;
-  float *dst = p.grad_value + ((row0 + py * W + px) * p.M + m) * p.D + cbeg;
+  float *dst = p.grad_value + ((row0 + py * W + px) * p.M + m) * p.D;
+  if (vec && (reinterpret_cast<uintptr_t>(p.grad_value) & 15u) == 0) {
+#pragma unroll
+    for (int q = 0; q < CS / 4; ++q)
+      *reinterpret_cast<float4 *>(dst + chan(4 * q)) =
+          make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+    return;
+  }
 #pragma unroll
   for (int c = 0; c < CS; ++c)
-    if (c < cnum) dst[c] = acc[c];
+    if (c < cnum) dst[chan(c)] = acc[c];
 }
 
 template <typename T, int CS>
