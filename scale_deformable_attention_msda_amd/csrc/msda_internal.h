@@ -77,7 +77,7 @@ struct Params {
                          // (sparse launches: no tile sort)
   int32_t seg_softmax;   // fused inputs: a pair's L*K logits sit in L*K consecutive lanes of
                          // the per-sample passes (L*K a power of two <= 64, one chunk)
-  int32_t ref_inblock;   // fused inputs: every workgroup holds whole queries (all M heads)
+  int32_t head_major;    // per-sample passes: a workgroup takes consecutive queries of one head
   // Fused inputs (ref_dim 2 or 4): loc then holds offsets, attn holds logits,
   // and grad_loc / grad_attn receive the offset and logit gradients.
   // ref_dim 0: loc and attn are the sampling core's own inputs.

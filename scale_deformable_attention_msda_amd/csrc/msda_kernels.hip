@@ -181,6 +181,35 @@ __device__ __forceinline__ uint32_t pair_base(const Params &p, uint32_t P) {
   return (n * (uint32_t)p.S * (uint32_t)p.M + m) * (uint32_t)p.D;
 }
 
+// The (n, q, m) pairs of one workgroup of a per-sample pass: pair g of the
+// workgroup is pair base + g * stride. Pair-major order (stride 1) takes ppb
+// consecutive pairs; head-major order (stride M) takes ppb consecutive queries
+// of one head, so that a workgroup's samples, and with the XCD-aware
+// numbering an XCD's, concentrate on one head's value channels.
+struct PairRange {
+  int64_t base;
+  int32_t stride, count;
+  __device__ int64_t operator()(int g) const { return base + (int64_t)g * stride; }
+};
+
+__device__ __forceinline__ PairRange block_pairs(const Params &p, int lb, int ppb) {
+  PairRange r;
+  if (p.head_major) {
+    const int qblocks = (p.Lq + ppb - 1) / ppb;
+    const int nm = lb / qblocks, qb = lb - nm * qblocks;
+    const int n = nm / p.M, m = nm - n * p.M;
+    const int q0 = qb * ppb;
+    r.base = ((int64_t)n * p.Lq + q0) * p.M + m;
+    r.stride = p.M;
+    r.count = min(ppb, p.Lq - q0);
+  } else {
+    r.base = (int64_t)lb * ppb;
+    r.stride = 1;
+    r.count = (int)min((int64_t)ppb, p.pairs - r.base);
+  }
+  return r;
+}
+
 // Exact quotient i / d for i < 1024 and 1 <= d <= 256 with mg = ceil(2^20 / d):
 // the rounding error of mg adds less than 2^-10 to i / d, whose fractional
 // part is 0 or at most 1 - 1/d.
@@ -298,16 +327,16 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(const Params p) {
   // descriptor rows padded by one so that consecutive samples of a pair (the
   // lanes that write them) fall on different LDS banks
   const int dstride = ppb + 1;
-  const int64_t P0 = (int64_t)xcd_remap(blockIdx.x, gridDim.x) * ppb;
-  const int npairs = (int)min((int64_t)ppb, p.pairs - P0);
+  const PairRange pr = block_pairs(p, xcd_remap(blockIdx.x, gridDim.x), ppb);
+  const int npairs = pr.count;
   const int g = tid / lpp;
   const int j = tid - g * lpp;
   const bool active = g < npairs;
-  if (tid < npairs) pbase[tid] = pair_base(p, (uint32_t)(P0 + tid));
+  if (tid < npairs) pbase[tid] = pair_base(p, (uint32_t)pr(tid));
   if constexpr (FUSE) {
-    if (tid < npairs) pqry[tid] = (uint32_t)(P0 + tid) / (uint32_t)p.M;
+    if (tid < npairs) pqry[tid] = (uint32_t)pr(tid) / (uint32_t)p.M;
     if (!p.seg_softmax) {
-      const float2 st = pair_softmax_stats<LPP>(p.attn + (active ? (P0 + g) * p.LK : 0), active, j, lpp, p.LK);
+      const float2 st = pair_softmax_stats<LPP>(p.attn + (active ? pr(g) * p.LK : 0), active, j, lpp, p.LK);
       if (active && j == 0) sst[g] = st;
     }
   }
@@ -337,7 +366,7 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(const Params p) {
       const int pp = i - gg * pcn;
       const int pt = pc0 + pp;
       const int l = (int)small_div((uint32_t)pt, kmg);
-      const int64_t gi = (P0 + gg) * p.LK + pt;
+      const int64_t gi = pr(gg) * p.LK + pt;
       const float2 v = *reinterpret_cast<const float2 *>(p.loc + 2 * gi);
       const float z = p.attn[gi];
       float2 xy = v;
@@ -377,7 +406,7 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(const Params p) {
     }
   }
   if (active) {
-    const int64_t obase = (P0 + g) * (int64_t)p.D;
+    const int64_t obase = pr(g) * (int64_t)p.D;
 #pragma unroll
     for (int cg = 0; cg < NCG; ++cg) {
       const int c = j + cg * lpp;
@@ -440,23 +469,22 @@ __device__ __forceinline__ void bwd_sample_body(const Params &p, int block, int 
   float2 *soff = reinterpret_cast<float2 *>(sst + kBlock);
   float *ssum = reinterpret_cast<float *>(soff + kDescCap);
   uint32_t *pqry = reinterpret_cast<uint32_t *>(ssum + kBlock);
-  float4 *sgr = reinterpret_cast<float4 *>(smem);  // reuses desc once the last chunk is done
   load_levels(p, sH, sW, sS);
 
   const int tid = threadIdx.x;
   const int lpp = LPP > 0 ? LPP : p.lpp;
   const int ppb = kBlock / lpp;
   const int dstride = ppb + 1;  // padded descriptor rows (see fwd_kernel)
-  const int64_t P0 = (int64_t)xcd_remap(block, nblocks) * ppb;
-  const int npairs = (int)min((int64_t)ppb, p.pairs - P0);
+  const PairRange pr = block_pairs(p, xcd_remap(block, nblocks), ppb);
+  const int npairs = pr.count;
   const int g = tid / lpp;
   const int j = tid - g * lpp;
   const bool active = g < npairs;
-  if (tid < npairs) pbase[tid] = pair_base(p, (uint32_t)(P0 + tid));
+  if (tid < npairs) pbase[tid] = pair_base(p, (uint32_t)pr(tid));
   if constexpr (FUSE) {
-    if (tid < npairs) pqry[tid] = (uint32_t)(P0 + tid) / (uint32_t)p.M;
+    if (tid < npairs) pqry[tid] = (uint32_t)pr(tid) / (uint32_t)p.M;
     if (!p.seg_softmax) {
-      const float2 st = pair_softmax_stats<LPP>(p.attn + (active ? (P0 + g) * p.LK : 0), active, j, lpp, p.LK);
+      const float2 st = pair_softmax_stats<LPP>(p.attn + (active ? pr(g) * p.LK : 0), active, j, lpp, p.LK);
       if (active && j == 0) sst[g] = st;
     }
   }
@@ -474,7 +502,7 @@ __device__ __forceinline__ void bwd_sample_body(const Params &p, int block, int 
   for (int cg = 0; cg < NCG; ++cg) {
     const int c = j + cg * lpp;
     lane_elem[cg] = c < nvec ? (uint32_t)(c * VEC) : kOobElem;
-    const uint32_t go = active && c < nvec ? (uint32_t)((P0 + g) * p.D + c * VEC) : kOobElem;
+    const uint32_t go = active && c < nvec ? (uint32_t)(pr(g) * p.D + c * VEC) : kOobElem;
     load_vals<T, VEC>(ro, go * (uint32_t)T::size, G[cg]);
   }
 
@@ -487,7 +515,7 @@ __device__ __forceinline__ void bwd_sample_body(const Params &p, int block, int 
       const int pp = i - gg * pcn;
       const int pt = pc0 + pp;
       const int l = (int)small_div((uint32_t)pt, kmg);
-      const int64_t gi = (P0 + gg) * p.LK + pt;
+      const int64_t gi = pr(gg) * p.LK + pt;
       const float2 v = *reinterpret_cast<const float2 *>(p.loc + 2 * gi);
       const float z = p.attn[gi];
       float2 xy = v;
@@ -577,7 +605,7 @@ __device__ __forceinline__ void bwd_sample_body(const Params &p, int block, int 
       const int gg = i / pcn;
       const int pp = i - gg * pcn;
       const float3 r = res[pp * dstride + gg];
-      const int64_t gi = (P0 + gg) * p.LK + pc0 + pp;
+      const int64_t gi = pr(gg) * p.LK + pc0 + pp;
       float2 gl = make_float2(r.y, r.z);
       float gz = r.x;
       if constexpr (FUSE) {
@@ -594,36 +622,19 @@ __device__ __forceinline__ void bwd_sample_body(const Params &p, int block, int 
     }
   }
   if constexpr (FUSE) {
-    const bool inblock = p.grad_ref && p.ref_inblock;
-    if (active && j == 0 && p.grad_ref) {
-      const float4 part = make_float4(acc_rx, acc_ry, acc_bx, acc_by);
-      if (inblock)
-        sgr[g] = part;
-      else
-        *reinterpret_cast<float4 *>(p.ws.ref_part + 4 * (P0 + g)) = part;
-    }
-    if (p.LK > p.pc || inblock) __syncthreads();
+    // the pair's share of its query's reference gradient (summed over the
+    // query's heads by ref_grad_kernel)
+    if (active && j == 0 && p.grad_ref)
+      *reinterpret_cast<float4 *>(p.ws.ref_part + 4 * pr(g)) = make_float4(acc_rx, acc_ry, acc_bx, acc_by);
     if (p.LK > p.pc) {
+      __syncthreads();
       // grad_logits from the grad_attn values this block stored above
       // (visible to the whole workgroup after the barrier)
       for (int i = tid; i < npairs * p.LK; i += kBlock) {
         const int gg = i / p.LK;
-        const int64_t gi = P0 * p.LK + i;
+        const int64_t gi = pr(gg) * p.LK + (i - gg * p.LK);
         const float A = softmax_weight(p.attn[gi], sst[gg]);
         p.grad_attn[gi] = A * (p.grad_attn[gi] - ssum[gg]);
-      }
-    }
-    if (inblock) {
-      // the block holds whole queries: sum the M pairs of each, in head order
-      const int nq = npairs / p.M;
-      for (int i = tid; i < nq * p.ref_dim; i += kBlock) {
-        const int qi = i / p.ref_dim, c = i - qi * p.ref_dim;
-        float sum = 0.0f;
-        for (int m = 0; m < p.M; ++m) {
-          const float4 v = sgr[qi * p.M + m];
-          sum += c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w;
-        }
-        p.grad_ref[(P0 / p.M + qi) * p.ref_dim + c] = sum;
       }
     }
   }
@@ -1200,23 +1211,32 @@ hipError_t launch_fn(const void *fn, int64_t blocks, int threads, int gy, Params
 }
 
 // Lane mapping and chunking of the per-sample passes (forward and the
-// backward's sample gradients).
-void set_sample_shape(Params &p, const LaunchShape &s) {
+// backward's sample gradients). The backward's sample pass takes head-major
+// workgroups: its value rows then stay in the L2 of the XCD that works on the
+// head (the inputs are warm after the binning passes). The forward, which
+// meets value cold, keeps pair-major workgroups, whose XCDs read whole pixel
+// rows (all heads) from HBM.
+void set_sample_shape(Params &p, const LaunchShape &s, bool backward) {
   p.lpp = s.lpp;
   const int ppb = kBlock / s.lpp;
   p.pc = min(p.LK, max(1, kDescCap / (ppb + 1)));
   const bool pow2 = (p.LK & (p.LK - 1)) == 0;
   p.seg_softmax = p.ref_dim != 0 && pow2 && p.LK <= 64 && p.LK <= p.pc ? 1 : 0;
-  p.ref_inblock = ppb % p.M == 0 ? 1 : 0;
+  p.head_major = backward ? 1 : 0;
+}
+
+// Workgroups of a per-sample pass.
+int64_t sample_blocks(const Params &p, int ppb) {
+  if (p.head_major) return (int64_t)p.N * p.M * ((p.Lq + ppb - 1) / ppb);
+  return (p.pairs + ppb - 1) / ppb;
 }
 
 hipError_t launch_pairs(bool fwd, const Params &p_in, DType dt, const LaunchShape &s, hipStream_t stream) {
   KernelFn fn = select(fwd, p_in.ref_dim != 0, dt, s);
   if (!fn) return hipErrorInvalidValue;
   Params p = p_in;
-  set_sample_shape(p, s);
-  const int ppb = kBlock / s.lpp;
-  const int64_t blocks = (p.pairs + ppb - 1) / ppb;
+  set_sample_shape(p, s, !fwd);
+  const int64_t blocks = sample_blocks(p, kBlock / s.lpp);
   return launch_fn(reinterpret_cast<const void *>(fn), blocks, kBlock, 1, p, stream);
 }
 
@@ -1302,7 +1322,7 @@ hipError_t launch_forward(const Params &p, DType dt, const LaunchShape &s, hipSt
 hipError_t launch_backward(const Params &p_in, DType dt, const LaunchShape &s, hipStream_t stream) {
   Params p = p_in;
   p.qpb = max(1, 1024 / p.LK);
-  set_sample_shape(p, s);
+  set_sample_shape(p, s, true);
   const bool fuse = p.ref_dim != 0;
   hipError_t e;
   // Sparse launches (few samples per 8x8 value tile, e.g. decoder queries): a
@@ -1342,13 +1362,13 @@ hipError_t launch_backward(const Params &p_in, DType dt, const LaunchShape &s, h
     while (cs < cs_need) cs *= 2;
     const int groups = (p.D + kChanGroup - 1) / kChanGroup;
     const int ppb = kBlock / s.lpp;
-    const int64_t sample_blocks = (p.pairs + ppb - 1) / ppb;
+    const int64_t nsample = sample_blocks(p, ppb);
     const bool hot_f32 = dt == DType::F32 && s.vec == 4 && s.lpp == 8 && s.ncg == 1 && cs == 8;
     const bool hot_bf16 = dt == DType::BF16 && s.vec == 8 && s.lpp == 4 && s.ncg == 1 && cs == 8;
     // grad_value blocks rounded to a multiple of 8 so that the sample blocks'
     // XCD-aware renumbering sees the hardware's block % 8 placement
     const int64_t gvb = (wmax + 7) & ~(int64_t)7;
-    if ((hot_f32 || hot_bf16) && groups == 1 && gvb + sample_blocks <= 0x7fffffff) {
+    if ((hot_f32 || hot_bf16) && groups == 1 && gvb + nsample <= 0x7fffffff) {
       p.gv_blocks = (int32_t)gvb;
       const void *fn;
       if (hot_f32)
@@ -1357,7 +1377,7 @@ hipError_t launch_backward(const Params &p_in, DType dt, const LaunchShape &s, h
       else
         fn = fuse ? reinterpret_cast<const void *>(bwd_fused_kernel<BF16, 8, 1, 4, 8, true>)
                   : reinterpret_cast<const void *>(bwd_fused_kernel<BF16, 8, 1, 4, 8, false>);
-      if ((e = launch_fn(fn, gvb + sample_blocks, kBlock, 1, p, stream)) != hipSuccess) return e;
+      if ((e = launch_fn(fn, gvb + nsample, kBlock, 1, p, stream)) != hipSuccess) return e;
     } else {
       if ((e = launch_pairs(false, p, dt, s, stream)) != hipSuccess) return e;
       KernelFn gv = dt == DType::F32 ? pick_gv<F32>(cs) : pick_gv<BF16>(cs);
@@ -1365,9 +1385,8 @@ hipError_t launch_backward(const Params &p_in, DType dt, const LaunchShape &s, h
         return e;
     }
   }
-  // 4. reference gradients (fused inputs, when asked for) of workgroups that
-  //    did not hold whole queries
-  if (fuse && p.grad_ref && !p.ref_inblock) {
+  // 4. reference gradients (fused inputs, when asked for)
+  if (fuse && p.grad_ref) {
     const int64_t n = p.pairs / p.M * p.ref_dim;
     return launch_fn(reinterpret_cast<const void *>(ref_grad_kernel), (n + kBlock - 1) / kBlock, kBlock, 1, p, stream);
   }
