@@ -142,6 +142,29 @@ def decoder_latency(msda, torch, dev, layers=6, reps=20):
     return res
 
 
+def copy_ceiling(torch, dev, reps=5):
+    """Measured stream-copy ceiling: a 512 MiB device-to-device copy whose source
+    and destination (1 GiB together) exceed the 256 MB Infinity Cache, timed with
+    HIP events; bytes read plus bytes written per second (median of reps)."""
+    import numpy as np
+
+    src = torch.ones(128 << 20, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    nbytes = 2 * src.numel() * 4
+    del src, dst
+    return nbytes / (float(np.median(ms)) * 1e-3) / 1e9
+
+
 def fused_passes(msda, torch, dev, steps, rotate):
     """The same encoder shape fed with raw predictions (reference points, pixel
     offsets, logits) through msda_fused_forward / msda_fused_backward, next to
@@ -354,6 +377,10 @@ def main():
 
     fwd = pass_stats(fwd_ms, b_fwd)
     bwd = pass_stats(bwd_ms, b_bwd)
+    copy_gbps = None if args.main_only else copy_ceiling(torch, dev)
+    if copy_gbps:
+        for st in (fwd, bwd):
+            st["frac_of_copy_ceiling"] = round(st["alg_GBps"] / copy_gbps, 4)
     traffic = measured_traffic()
     dom, dom_name, dom_b = (bwd, "bwd", b_bwd) if bwd["us_mean"] >= fwd["us_mean"] else (fwd, "fwd", b_fwd)
     achieved = dom_b / (dom["us_mean"] * 1e-6) / 1e9
@@ -373,6 +400,7 @@ def main():
                    "points_per_step": pts, "buffer_sets_cycled": args.rotate},
         "roofline": roofline,
         "fwd": fwd, "bwd": bwd,
+        "copy_ceiling_GBps": None if copy_gbps is None else round(copy_gbps, 1),
         "kernel_source_sha256": kernel_source_hash(),
     }
     if not args.main_only:

@@ -12,7 +12,8 @@ import pytest
 
 torch = pytest.importorskip("torch")
 
-from oracle import msda_backward, msda_forward, msda_grad_value_rows  # noqa: E402
+from oracle import (fused_locations, msda_backward, msda_forward, msda_fused_backward,  # noqa: E402
+                    msda_grad_value_rows, softmax_weights)
 from tests.gpu_util import (assert_f32, assert_grad_loc, assert_normwise, bf16_ulp,  # noqa: E402
                             device_inputs, gpu_backward, gpu_forward, max_abs, note, sample_pairs,
                             sample_rows, to_f64)
@@ -409,3 +410,62 @@ def test_graph_capture_of_decoder_layers():
                 assert torch.equal(a, b), (rep, k)
             else:
                 assert torch.allclose(a, b, rtol=0, atol=1e-5), (rep, k)
+
+
+def test_batch_split_across_launches():
+    """Images whose value slice exceeds 2^27 elements run one launch per image;
+    every pointer (value, loc, attn, ref, outputs and gradients) is offset per
+    launch and the workspace is reused. One level of 1449x1449 pixels, M=2,
+    D=32: 134.4 M elements per image, so N=3 takes three launches."""
+    rng = np.random.default_rng(990)
+    N, H, W, M, D, K, Lq = 3, 1449, 1449, 2, 32, 4, 150
+    S = H * W
+    shapes = np.array([[H, W]], dtype=np.int64)
+    starts = np.array([0], dtype=np.int64)
+    value = rng.standard_normal((N, S, M, D), dtype=np.float32)
+    loc = rng.uniform(-0.05, 1.05, (N, Lq, M, 1, K, 2)).astype(np.float32)
+    attn = rng.uniform(0, 1, (N, Lq, M, 1, K)).astype(np.float32)
+    G = rng.standard_normal((N, Lq, M, D), dtype=np.float32)
+    note("batch split: N=3 images of 1449x1449 x M=2 x D=32, one launch per image")
+    dv = torch.from_numpy(value).cuda()
+    dl, da, dg = (torch.from_numpy(a).cuda() for a in (loc, attn, G))
+    out = msda.msda_forward(dv, shapes, starts, dl, da)
+    gv, gl, ga = msda.msda_backward(dv, shapes, starts, dl, da, dg)
+    torch.cuda.synchronize()
+    n = np.repeat(np.arange(N), 40)
+    q = np.tile(np.linspace(0, Lq - 1, 40).astype(np.int64), N)
+    m = np.tile(np.arange(40) % M, N)
+    idx = (torch.as_tensor(n), torch.as_tensor(q), torch.as_tensor(m))
+    assert_f32("out", to_f64(out[idx]), msda_forward(value, shapes, starts, loc, attn, pairs=(n, q, m)))
+    _, rgl, rga = msda_backward(value, shapes, starts, loc, attn, G, pairs=(n, q, m), with_grad_value=False)
+    assert_f32("grad_attn", to_f64(ga[idx]), rga)
+    assert_grad_loc(to_f64(gl[idx]), rgl, shapes)
+    # grad_value rows: ones that samples touch (corner pixels of sampled pairs) and random ones
+    px = np.clip((loc[n, q, m, 0, 0, 0] * W - 0.5).astype(np.int64), 0, W - 1)
+    py = np.clip((loc[n, q, m, 0, 0, 1] * H - 0.5).astype(np.int64), 0, H - 1)
+    rs = np.concatenate([py * W + px, rng.integers(0, S, 60)])
+    rn = np.concatenate([n, rng.integers(0, N, 60)])
+    rm = np.concatenate([m, rng.integers(0, M, 60)])
+    rgv = msda_grad_value_rows(value, shapes, starts, loc, attn, G, (rn, rs, rm))
+    assert np.abs(rgv).max() > 0
+    assert_f32("grad_value", to_f64(gv[torch.as_tensor(rn), torch.as_tensor(rs), torch.as_tensor(rm)]), rgv)
+    # the fused entry points split the same way (ref and grad_ref offset per launch)
+    ref = rng.uniform(0.2, 0.8, (N, Lq, 4)).astype(np.float32)
+    ref[..., 2:] = rng.uniform(0.05, 0.3, (N, Lq, 2))
+    off = rng.standard_normal((N, Lq, M, 1, K, 2)).astype(np.float32) * 0.3
+    z = rng.standard_normal((N, Lq, M, 1, K)).astype(np.float32)
+    dref, doff, dz = (torch.from_numpy(a).cuda() for a in (ref, off, z))
+    fout = msda.msda_fused_forward(dv, shapes, starts, dref, doff, dz)
+    _, fgo, fgz, fgr = msda.msda_fused_backward(dv, shapes, starts, dref, doff, dz, dg)
+    torch.cuda.synchronize()
+    floc = fused_locations(ref, off, shapes)
+    fA = softmax_weights(z)
+    assert_f32("fused out", to_f64(fout[idx]), msda_forward(value, shapes, starts, floc, fA, pairs=(n, q, m)))
+    qn, qq = np.arange(N).repeat(3), np.tile(np.array([0, Lq // 2, Lq - 1]), N)
+    _, rgo, rgz, rgr = msda_fused_backward(value, shapes, starts, ref, off, z, G, queries=(qn, qq))
+    qi = (torch.as_tensor(qn), torch.as_tensor(qq))
+    assert_f32("fused grad_logits", to_f64(fgz[qi]), rgz)
+    scale = (np.float64(W) * ref[qn, qq, 2:][:, None, None, None, :])  # box size * W_l: pixel units
+    assert_f32("fused grad_offsets (pixel units)", to_f64(fgo[qi]) / scale, rgo / scale)
+    bound = 1e-5 * M * K * W * (1 + np.abs(off).max())
+    assert max_abs(to_f64(fgr[qi]), rgr) <= bound
