@@ -70,7 +70,8 @@ struct Params {
   uint32_t value_elems;  // elements of value in this launch (< kOobElem)
   int32_t TPI;           // tiles per (image, head) over all levels
   int32_t T;             // tiles of the launch: N * M * TPI
-  int32_t qpb;           // queries per workgroup of the binning passes
+  int32_t qpb;           // queries per workgroup of the scatter (binning) pass
+  int32_t qpb0;          // queries per workgroup of the counting (binning) pass
   int32_t gvec;          // grad_out rows allow 16-byte loads
   int32_t gv_blocks;     // grad_value blocks of the fused backward launch
   int32_t scatter;       // grad_value zero-filled, then added to with float atomics per sample

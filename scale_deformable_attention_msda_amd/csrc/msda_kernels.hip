@@ -210,9 +210,9 @@ __device__ __forceinline__ PairRange block_pairs(const Params &p, int lb, int pp
   return r;
 }
 
-// Exact quotient i / d for i < 1024 and 1 <= d <= 256 with mg = ceil(2^20 / d):
-// the rounding error of mg adds less than 2^-10 to i / d, whose fractional
-// part is 0 or at most 1 - 1/d.
+// Exact quotient i / d for 1 <= d <= 256 and i * d <= 2^20 (so any i < 4096)
+// with mg = ceil(2^20 / d): the rounding error of mg adds less than i / 2^20
+// <= 1/d to i / d, whose fractional part is 0 or at most 1 - 1/d.
 __device__ __forceinline__ uint32_t small_div(uint32_t i, uint32_t mg) { return (i * mg) >> 20; }
 __device__ __forceinline__ uint32_t small_magic(uint32_t d) { return ((1u << 20) + d - 1) / d; }
 
@@ -361,31 +361,45 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(const Params p) {
     const int pcn = min(p.pc, p.LK - pc0);
     const uint32_t pmg = small_magic((uint32_t)pcn);
     __syncthreads();
-    for (int i = tid; i < npairs * pcn; i += kBlock) {
-      const int gg = (int)small_div((uint32_t)i, pmg);
-      const int pp = i - gg * pcn;
-      const int pt = pc0 + pp;
-      const int l = (int)small_div((uint32_t)pt, kmg);
-      const int64_t gi = pr(gg) * p.LK + pt;
-      const float2 v = *reinterpret_cast<const float2 *>(p.loc + 2 * gi);
-      const float z = p.attn[gi];
-      float2 xy = v;
-      float A = z;
-      if constexpr (FUSE) {
-        xy = form_loc<true>(p, v, l, load_ref(p, pqry[gg]), sH, sW);
-        A = p.seg_softmax ? segment_softmax(z, p.LK) : softmax_weight(z, sst[gg]);
-      }
-      const Sample s = sample_geometry(p, pbase[gg], xy, A, l, sH, sW, sS);
-      FDesc d;
-      const float wa[2] = {1.0f - s.a, s.a};
-      const float wb[2] = {1.0f - s.b, s.b};
+    // two samples per thread per round, both samples' loads issued first
+    const int total = npairs * pcn;
+    for (int i0 = tid; i0 < total; i0 += 2 * kBlock) {
+      float2 v[2];
+      float z[2];
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const bool ok = s.off[c] != kOobElem;
-        d.off[c] = s.off[c] * (uint32_t)T::size;
-        d.w[c] = ok ? s.A * wb[c >> 1] * wa[c & 1] : 0.0f;
+      for (int u = 0; u < 2; ++u) {
+        const int i = i0 + u * kBlock;
+        const int gg = (int)small_div((uint32_t)(i < total ? i : 0), pmg);
+        const int64_t gi = pr(gg) * p.LK + pc0 + ((i < total ? i : 0) - gg * pcn);
+        v[u] = i < total ? *reinterpret_cast<const float2 *>(p.loc + 2 * gi) : make_float2(0.0f, 0.0f);
+        z[u] = i < total ? p.attn[gi] : 0.0f;
       }
-      desc[pp * dstride + gg] = d;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int i = i0 + u * kBlock;
+        if (i >= total) continue;  // whole pairs of samples drop out together
+        const int gg = (int)small_div((uint32_t)i, pmg);
+        const int pp = i - gg * pcn;
+        const int pt = pc0 + pp;
+        const int l = (int)small_div((uint32_t)pt, kmg);
+        float2 xy = v[u];
+        float A = z[u];
+        if constexpr (FUSE) {
+          xy = form_loc<true>(p, v[u], l, load_ref(p, pqry[gg]), sH, sW);
+          A = p.seg_softmax ? segment_softmax(z[u], p.LK) : softmax_weight(z[u], sst[gg]);
+        }
+        const Sample s = sample_geometry(p, pbase[gg], xy, A, l, sH, sW, sS);
+        FDesc d;
+        const float wa[2] = {1.0f - s.a, s.a};
+        const float wb[2] = {1.0f - s.b, s.b};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const bool ok = s.off[c] != kOobElem;
+          d.off[c] = s.off[c] * (uint32_t)T::size;
+          d.w[c] = ok ? s.A * wb[c >> 1] * wa[c & 1] : 0.0f;
+        }
+        desc[pp * dstride + gg] = d;
+      }
     }
     __syncthreads();
     if (active) {
@@ -710,7 +724,11 @@ __global__ __launch_bounds__(kBlock) void bin_kernel(const Params p) {
   __shared__ int32_t sH[kMaxLevels], sW[kMaxLevels], sS[kMaxLevels], sTW[kMaxLevels], sToff[kMaxLevels];
   load_tile_levels(p, sH, sW, sS, sTW, sToff);
   const int tid = threadIdx.x;
-  const int qblocks = (p.Lq + p.qpb - 1) / p.qpb;
+  // the counting pass takes 8 samples per thread (it keeps no per-sample
+  // state), the scatter pass 4
+  constexpr int NS = MODE == 0 ? 8 : 4;
+  const int qpb = MODE == 0 ? p.qpb0 : p.qpb;
+  const int qblocks = (p.Lq + qpb - 1) / qpb;
   const int bin_blocks = p.N * p.M * qblocks;
   if (MODE == 1 && (int)blockIdx.x >= bin_blocks) {
     // the scatter launch carries extra workgroups that clear the split tiles
@@ -721,8 +739,8 @@ __global__ __launch_bounds__(kBlock) void bin_kernel(const Params p) {
   const int nm = blockIdx.x / qblocks;
   const int qb = blockIdx.x - nm * qblocks;
   const int n = nm / p.M, m = nm - n * p.M;
-  const int q0 = qb * p.qpb;
-  const int nsamp = (min(p.Lq, q0 + p.qpb) - q0) * p.LK;
+  const int q0 = qb * qpb;
+  const int nsamp = (min(p.Lq, q0 + qpb) - q0) * p.LK;
   const uint32_t tbase = ((uint32_t)m * (uint32_t)p.N + (uint32_t)n) * (uint32_t)p.TPI;
   const bool local = p.TPI <= kBinCap;
   uint4 *rec_out = reinterpret_cast<uint4 *>(p.ws.entries);
@@ -749,29 +767,42 @@ __global__ __launch_bounds__(kBlock) void bin_kernel(const Params p) {
   }
   __syncthreads();
 
+  // The thread's four samples: all their loads first (one round trip), then
+  // the tile walk. Sample i is (query qi = i / LK, point pt = i % LK).
+  const uint32_t lkmg = small_magic((uint32_t)p.LK), kmg = small_magic((uint32_t)p.K);
+  float2 xyv[NS];
+  float av[NS];
+#pragma unroll
+  for (int r = 0; r < NS; ++r) {
+    const int i = tid + r * kBlock;
+    const bool ok = i < nsamp;
+    const int qi = (int)small_div((uint32_t)(ok ? i : 0), lkmg);
+    const int pt = (ok ? i : 0) - qi * p.LK;
+    const int64_t sid = (((int64_t)n * p.Lq + q0 + qi) * p.M + m) * p.LK + pt;
+    xyv[r] = ok ? *reinterpret_cast<const float2 *>(p.loc + 2 * sid) : make_float2(0.0f, 0.0f);
+    av[r] = MODE == 1 && ok ? p.attn[sid] : 0.0f;
+  }
   // Up to four tiles per sample, in fixed slots (dy, dx) so that every array
   // index below is a compile-time constant.
-  uint4 rec[4];
-  uint32_t tl[4][4], rk[4][4];
-  bool has[4][4];
+  uint4 rec[NS];
+  uint32_t tl[NS][4], rk[NS][4];
+  bool has[NS][4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
+  for (int r = 0; r < NS; ++r) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) has[r][k] = false;
     const int i = tid + r * kBlock;
     if (i >= nsamp) continue;
-    const int qi = i / p.LK;
+    const int qi = (int)small_div((uint32_t)i, lkmg);
     const int pt = i - qi * p.LK;
     const uint32_t P = (uint32_t)(((int64_t)n * p.Lq + q0 + qi) * p.M + m);
-    const int64_t sid = (int64_t)P * p.LK + pt;
-    const int l = pt / p.K;
-    float2 xy = *reinterpret_cast<const float2 *>(p.loc + 2 * sid);
+    const int l = (int)small_div((uint32_t)pt, kmg);
+    float2 xy = xyv[r];
     if constexpr (FUSE) xy = form_loc<true>(p, xy, l, load_ref(p, (uint32_t)(n * p.Lq + q0 + qi)), sH, sW);
-    float A = 0.0f;
-    if constexpr (MODE == 1) {
-      A = p.attn[sid];
+    float A = av[r];
+    if constexpr (MODE == 1 && FUSE) {
       // before the branch below: every lane of the pair takes part
-      if constexpr (FUSE) A = seg ? segment_softmax(A, p.LK) : softmax_weight(A, bst[qi]);
+      A = seg ? segment_softmax(A, p.LK) : softmax_weight(A, bst[qi]);
     }
     Footprint f;
     if (!sample_footprint(xy.x, xy.y, sH[l], sW[l], f)) continue;
@@ -815,7 +846,7 @@ __global__ __launch_bounds__(kBlock) void bin_kernel(const Params p) {
     }
     __syncthreads();
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int r = 0; r < NS; ++r)
 #pragma unroll
       for (int k = 0; k < 4; ++k)
         if (has[r][k]) rec_out[gbase[tl[r][k]] + rk[r][k]] = rec[r];
@@ -1322,6 +1353,7 @@ hipError_t launch_forward(const Params &p, DType dt, const LaunchShape &s, hipSt
 hipError_t launch_backward(const Params &p_in, DType dt, const LaunchShape &s, hipStream_t stream) {
   Params p = p_in;
   p.qpb = max(1, 1024 / p.LK);
+  p.qpb0 = max(1, 2048 / p.LK);
   set_sample_shape(p, s, true);
   const bool fuse = p.ref_dim != 0;
   hipError_t e;
@@ -1347,11 +1379,12 @@ hipError_t launch_backward(const Params &p_in, DType dt, const LaunchShape &s, h
     // 2. counting sort of (sample, tile) entries; the scatter launch also clears
     //    the tiles whose grad_value is summed over several work items
     const int64_t bin_blocks = (int64_t)p.N * p.M * ((p.Lq + p.qpb - 1) / p.qpb);
+    const int64_t bin0_blocks = (int64_t)p.N * p.M * ((p.Lq + p.qpb0 - 1) / p.qpb0);
     const void *bin0 = fuse ? reinterpret_cast<const void *>(bin_kernel<0, true>)
                             : reinterpret_cast<const void *>(bin_kernel<0, false>);
     const void *bin1 = fuse ? reinterpret_cast<const void *>(bin_kernel<1, true>)
                             : reinterpret_cast<const void *>(bin_kernel<1, false>);
-    if ((e = launch_fn(bin0, bin_blocks, kBlock, 1, p, stream)) != hipSuccess) return e;
+    if ((e = launch_fn(bin0, bin0_blocks, kBlock, 1, p, stream)) != hipSuccess) return e;
     if ((e = launch_fn(reinterpret_cast<const void *>(scan_kernel), 1, 1024, 1, p, stream)) != hipSuccess) return e;
     if ((e = launch_fn(bin1, bin_blocks + 256, kBlock, 1, p, stream)) != hipSuccess) return e;
     // 3. grad_value per tile, and grad_attn / grad_loc per sample
