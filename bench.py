@@ -187,8 +187,9 @@ def fused_passes(msda, torch, dev, steps, rotate):
         s["go"] = torch.empty_like(s["off"])
         s["gz"] = torch.empty_like(s["logits"])
         s["gr"] = torch.empty_like(s["ref"])
-        s["ws"] = torch.empty(msda.msda_backward_workspace_size(ss, ls, d["N"], d["S"], d["M"], d["D"], d["L"],
-                                                                d["Lq"], d["K"]), dtype=torch.uint8, device=dev)
+        s["ws"] = torch.empty(msda.msda_fused_backward_workspace_size(ss, ls, d["N"], d["S"], d["M"], d["D"],
+                                                                      d["L"], d["Lq"], d["K"]),
+                              dtype=torch.uint8, device=dev)
         sets.append(s)
 
     def fwd(s):
@@ -203,10 +204,27 @@ def fused_passes(msda, torch, dev, steps, rotate):
         loc = s["ref"][:, :, None, None, None, :] + s["off"] / size[None, None, None, :, None, :]
         msda.msda_forward(s["value"], ss, ls, loc, attn, out=s["out"])
 
+    # the unfused route's backward: weights and locations saved by its forward,
+    # the core backward, then the softmax and location gradients as torch ops
+    for st in sets:
+        st["attn"] = torch.softmax(st["logits"].reshape(d["N"], d["Lq"], d["M"], -1), -1).reshape(
+            st["logits"].shape).contiguous()
+        st["loc"] = (st["ref"][:, :, None, None, None, :] + st["off"] / size[None, None, None, :, None, :]).contiguous()
+        st["ws_core"] = torch.empty(msda.msda_backward_workspace_size(ss, ls, d["N"], d["S"], d["M"], d["D"], d["L"],
+                                                                      d["Lq"], d["K"]), dtype=torch.uint8, device=dev)
+
+    def unfused_bwd(s):
+        gv, gl, ga = msda.msda_backward(s["value"], ss, ls, s["loc"], s["attn"], s["g"], grad_value=s["gv"],
+                                        workspace=s["ws_core"])
+        a = s["attn"]
+        torch.mul(a, ga - (a * ga).sum(dim=(-2, -1), keepdim=True), out=s["gz"])
+        torch.div(gl, size[None, None, None, :, None, :], out=s["go"])
+        torch.sum(gl, dim=(2, 3, 4), out=s["gr"])
+
     stream = torch.cuda.current_stream()
     res = {"workload": "encoder shape as above from raw inputs: reference points at pixel centres, "
                        "N(0,2px) offsets, N(0,1) logits"}
-    for name, fn in (("fwd", fwd), ("bwd", bwd), ("unfused_fwd", unfused_fwd)):
+    for name, fn in (("fwd", fwd), ("bwd", bwd), ("unfused_fwd", unfused_fwd), ("unfused_bwd", unfused_bwd)):
         for i in range(3):
             fn(sets[i % rotate])
         torch.cuda.synchronize()

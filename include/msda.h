@@ -105,12 +105,11 @@ msda_status msda_forward(const void *value, const int64_t *spatial_shapes,
                          int64_t Lq, int64_t K, int dtype, hipStream_t stream);
 
 /*
- * Bytes of device workspace msda_backward and msda_fused_backward need for
- * these sizes (the same checks as msda_validate apply). The workspace holds a
- * counting sort of the samples by the 8x8-pixel tile of the value map they
- * touch: a few counters per tile plus up to four 16-byte entries per sample,
- * and 16 bytes per (image, query, head) for the fused variant, about
- * 64*N*Lq*M*L*K + 16*N*Lq*M bytes.
+ * Bytes of device workspace msda_backward needs for these sizes (the same
+ * checks as msda_validate apply). The workspace holds a counting sort of the
+ * samples by the 8x8-pixel tile of the value map they touch: a few counters
+ * per tile plus up to four 16-byte entries per sample, about 64*N*Lq*M*L*K
+ * bytes.
  */
 msda_status msda_backward_workspace_size(const int64_t *spatial_shapes, const int64_t *level_start,
                                          int64_t N, int64_t S, int64_t M, int64_t D, int64_t L,
@@ -186,9 +185,20 @@ msda_status msda_fused_forward(const void *value, const int64_t *spatial_shapes,
  * grad_value [N,S,M,D], grad_offsets [N,Lq,M,L,K,2] (8-byte aligned),
  * grad_logits [N,Lq,M,L,K] and grad_ref [N,Lq,ref_dim] are float32 and
  * overwritten. grad_ref may be NULL (then it is not computed: reference
- * points are often detached between layers). Workspace, determinism (all but
- * grad_value are deterministic), errors and asynchrony as for msda_backward.
+ * points are often detached between layers). The workspace must hold
+ * msda_fused_backward_workspace_size bytes; determinism (all but grad_value
+ * are deterministic), errors and asynchrony as for msda_backward.
  */
+/*
+ * Bytes of device workspace msda_fused_backward needs: the above plus 12 bytes
+ * per sample (the locations and weights formed from the raw predictions) and
+ * 16 bytes per (image, query, head) (reference-gradient partial sums).
+ */
+msda_status msda_fused_backward_workspace_size(const int64_t *spatial_shapes,
+                                               const int64_t *level_start, int64_t N, int64_t S,
+                                               int64_t M, int64_t D, int64_t L, int64_t Lq, int64_t K,
+                                               int dtype, size_t *bytes);
+
 msda_status msda_fused_backward(const void *value, const int64_t *spatial_shapes,
                                 const int64_t *level_start, const float *ref, int ref_dim,
                                 const float *offsets, const float *logits, const void *grad_out,

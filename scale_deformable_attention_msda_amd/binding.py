@@ -56,6 +56,8 @@ def load_library():
     lib.msda_fused_forward.restype = ci
     lib.msda_fused_backward.argtypes = [vp] * 4 + [ci] + [vp] * 7 + [i64] * 7 + [ci, vp, ctypes.c_size_t, vp]
     lib.msda_fused_backward.restype = ci
+    lib.msda_fused_backward_workspace_size.argtypes = [vp, vp] + [i64] * 7 + [ci, ctypes.POINTER(ctypes.c_size_t)]
+    lib.msda_fused_backward_workspace_size.restype = ci
     lib.msda_grouped_forward.argtypes = [vp] * 6 + [i64] * 8 + [ci, vp]
     lib.msda_grouped_forward.restype = ci
     lib.msda_grouped_backward.argtypes = [vp] * 9 + [i64] * 8 + [ci, vp, ctypes.c_size_t, vp]
@@ -160,6 +162,16 @@ def msda_backward_workspace_size(spatial_shapes, level_start, N, S, M, D, L, Lq,
     out = ctypes.c_size_t(0)
     _raise(load_library().msda_backward_workspace_size(ss.ctypes.data, ls.ctypes.data, N, S, M, D, L, Lq,
                                                        K, dtype, ctypes.byref(out)))
+    return out.value
+
+
+def msda_fused_backward_workspace_size(spatial_shapes, level_start, N, S, M, D, L, Lq, K, dtype=MSDA_F32):
+    """Bytes of device workspace msda_fused_backward needs for these sizes."""
+    ss = _host_i64(spatial_shapes, (L, 2), "spatial_shapes")
+    ls = _host_i64(level_start, (L,), "level_start")
+    out = ctypes.c_size_t(0)
+    _raise(load_library().msda_fused_backward_workspace_size(ss.ctypes.data, ls.ctypes.data, N, S, M, D, L, Lq,
+                                                             K, dtype, ctypes.byref(out)))
     return out.value
 
 
@@ -283,7 +295,7 @@ def msda_fused_backward(value, spatial_shapes, level_start, ref, offsets, logits
         _device_tensor(t, name, torch.float32)
         if tuple(t.shape) != shape:
             raise ValueError(f"{name} must be {shape}")
-    need = msda_backward_workspace_size(ss, ls, N, S, G, M // G * D, L, Lq, K, dt)
+    need = msda_fused_backward_workspace_size(ss, ls, N, S, G, M // G * D, L, Lq, K, dt)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     else:

@@ -99,7 +99,8 @@ msda_status backward_impl(const void *value, const int64_t *spatial_shapes, cons
   if (!aligned(grad_value, 4)) return MSDA_ERROR_MISALIGNED;
   const int64_t esz = elem_size(dtype);
   const int64_t step = images_per_launch(S, M, D, Lq, L, K);
-  const msda::WorkspaceLayout wl = msda::workspace_layout(spatial_shapes, L, std::min(step, N), M, Lq, K);
+  const msda::WorkspaceLayout wl =
+      msda::workspace_layout(spatial_shapes, L, std::min(step, N), M, Lq, K, ref_dim != 0);
   if (Lq > 0) {
     if (!value || !loc || !attn || !grad_out || !grad_loc || !grad_attn || (ref_dim && !ref))
       return MSDA_ERROR_INVALID_VALUE;
@@ -132,6 +133,8 @@ msda_status backward_impl(const void *value, const int64_t *spatial_shapes, cons
   p.ws.split_list = reinterpret_cast<uint32_t *>(ws + wl.off_split);
   p.ws.entries = reinterpret_cast<uint32_t *>(ws + wl.off_entries);
   p.ws.ref_part = reinterpret_cast<float *>(ws + wl.off_refpart);
+  p.ws.floc = reinterpret_cast<float *>(ws + wl.off_floc);
+  p.ws.fattn = reinterpret_cast<float *>(ws + wl.off_fattn);
   for (int64_t n0 = 0; n0 < N; n0 += step) {
     const int64_t nb = std::min(step, N - n0);
     p.N = (int32_t)nb;
@@ -141,6 +144,8 @@ msda_status backward_impl(const void *value, const int64_t *spatial_shapes, cons
     p.value = static_cast<const char *>(value) + n0 * S * M * D * esz;
     p.loc = loc + n0 * Lq * M * L * K * 2;
     p.attn = attn + n0 * Lq * M * L * K;
+    p.offsets = ref_dim ? p.loc : nullptr;  // fused inputs: the raw predictions
+    p.logits = ref_dim ? p.attn : nullptr;
     p.ref = ref_dim ? ref + n0 * Lq * ref_dim : nullptr;
     p.grad_out = static_cast<const char *>(grad_out) + n0 * Lq * M * D * esz;
     p.grad_value = grad_value + n0 * S * M * D;
@@ -213,7 +218,18 @@ msda_status msda_backward_workspace_size(const int64_t *spatial_shapes, const in
   msda_status st = msda_validate(spatial_shapes, level_start, N, S, M, D, L, Lq, K, dtype);
   if (st != MSDA_SUCCESS) return st;
   const int64_t step = std::min(std::max<int64_t>(N, 1), images_per_launch(S, M, D, Lq, L, K));
-  *bytes = msda::workspace_layout(spatial_shapes, L, step, M, Lq, K).bytes;
+  *bytes = msda::workspace_layout(spatial_shapes, L, step, M, Lq, K, false).bytes;
+  return MSDA_SUCCESS;
+}
+
+msda_status msda_fused_backward_workspace_size(const int64_t *spatial_shapes, const int64_t *level_start, int64_t N,
+                                               int64_t S, int64_t M, int64_t D, int64_t L, int64_t Lq, int64_t K,
+                                               int dtype, size_t *bytes) {
+  if (!bytes) return MSDA_ERROR_INVALID_VALUE;
+  msda_status st = msda_validate(spatial_shapes, level_start, N, S, M, D, L, Lq, K, dtype);
+  if (st != MSDA_SUCCESS) return st;
+  const int64_t step = std::min(std::max<int64_t>(N, 1), images_per_launch(S, M, D, Lq, L, K));
+  *bytes = msda::workspace_layout(spatial_shapes, L, step, M, Lq, K, true).bytes;
   return MSDA_SUCCESS;
 }
 

@@ -50,6 +50,8 @@ struct Workspace {
   uint32_t *split_list;   // [T] tiles whose entries span several work items
   uint32_t *entries;      // [4*Emax] (sample, tile) entries, tile-major, 16-byte records
   float *ref_part;        // [4*pairs] per-pair sums of the reference gradient (fused inputs)
+  float *floc;            // [2*samples] locations formed from the fused inputs
+  float *fattn;           // [samples] weights formed from the fused inputs
 };
 
 // One launch covers images [0, N) of the pointers below (the host offsets the
@@ -83,6 +85,8 @@ struct Params {
   // and grad_loc / grad_attn receive the offset and logit gradients.
   // ref_dim 0: loc and attn are the sampling core's own inputs.
   const float *ref;      // [pairs / M, ref_dim] reference points or boxes
+  const float *offsets;  // backward with fused inputs: the raw offsets and logits
+  const float *logits;   // (loc and attn then point at the formed ones)
   int32_t ref_dim;
   float *grad_ref;       // [pairs / M, ref_dim], may be null
   Workspace ws;
@@ -105,10 +109,11 @@ LaunchShape choose_shape(int D, DType dt, uintptr_t align_bits, int64_t pairs);
 // Tile table and workspace layout of a launch covering `nimg` images.
 struct WorkspaceLayout {
   int64_t T, Wmax, Emax;
-  size_t off_count, off_cursor, off_start, off_witem, off_nwork, off_split, off_entries, off_refpart, bytes;
+  size_t off_count, off_cursor, off_start, off_witem, off_nwork, off_split, off_entries, off_refpart, off_floc,
+      off_fattn, bytes;
 };
 WorkspaceLayout workspace_layout(const int64_t *spatial_shapes, int64_t L, int64_t nimg, int64_t M,
-                                 int64_t Lq, int64_t K);
+                                 int64_t Lq, int64_t K, bool fused);
 void fill_tiles(LevelTable &lv, const int64_t *spatial_shapes, int64_t L, int32_t *TPI);
 
 hipError_t launch_forward(const Params &p, DType dt, const LaunchShape &s, hipStream_t stream);

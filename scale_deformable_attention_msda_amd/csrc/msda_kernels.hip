@@ -455,16 +455,17 @@ struct __align__(16) BDesc {
 
 constexpr size_t kSampleSmemPlain =
     kDescCap * (sizeof(BDesc) + sizeof(float3) + 4) + 3 * kMaxLevels * 4 + kBlock * 4;
-// fused inputs add per pair: softmax statistics, sum of A * grad_attn, query
-// row; per staged sample: its offset
-constexpr size_t kSampleSmemFused = kSampleSmemPlain + kBlock * (8 + 4 + 4) + kDescCap * 8;
+// fused inputs add per pair: sum of A * grad_attn, query row; per staged
+// sample: its offset
+constexpr size_t kSampleSmemFused = kSampleSmemPlain + kBlock * (4 + 4) + kDescCap * 8;
 template <bool FUSE>
 constexpr size_t sample_smem() { return FUSE ? kSampleSmemFused : kSampleSmemPlain; }
 
 // grad_attn and grad_loc of the pairs of logical block `block` (of `nblocks`),
 // with LDS carved from `smem` (sample_smem<FUSE>() bytes). With p.scatter the
 // same pass also adds each sample's grad_value contributions (attn * corner
-// weight * grad_out) with float atomics. With fused inputs grad_attn and
+// weight * grad_out) with float atomics. With fused inputs (loc and attn then
+// hold the locations and weights that fused_inputs_kernel formed) grad_attn and
 // grad_loc become the logit and offset gradients: through the softmax,
 // d/dz_i = A_i (grad_attn_i - sum_j A_j grad_attn_j); through the location,
 // d/d offset = grad_loc / size (points) or grad_loc * box size (boxes); and the
@@ -479,8 +480,7 @@ __device__ __forceinline__ void bwd_sample_body(const Params &p, int block, int 
   int32_t *sW = sH + kMaxLevels, *sS = sW + kMaxLevels;
   uint32_t *pbase = reinterpret_cast<uint32_t *>(sS + kMaxLevels);
   // fused inputs only
-  float2 *sst = reinterpret_cast<float2 *>(smem + kSampleSmemPlain);
-  float2 *soff = reinterpret_cast<float2 *>(sst + kBlock);
+  float2 *soff = reinterpret_cast<float2 *>(smem + kSampleSmemPlain);
   float *ssum = reinterpret_cast<float *>(soff + kDescCap);
   uint32_t *pqry = reinterpret_cast<uint32_t *>(ssum + kBlock);
   load_levels(p, sH, sW, sS);
@@ -497,10 +497,6 @@ __device__ __forceinline__ void bwd_sample_body(const Params &p, int block, int 
   if (tid < npairs) pbase[tid] = pair_base(p, (uint32_t)pr(tid));
   if constexpr (FUSE) {
     if (tid < npairs) pqry[tid] = (uint32_t)pr(tid) / (uint32_t)p.M;
-    if (!p.seg_softmax) {
-      const float2 st = pair_softmax_stats<LPP>(p.attn + (active ? pr(g) * p.LK : 0), active, j, lpp, p.LK);
-      if (active && j == 0) sst[g] = st;
-    }
   }
   // the pair's sums over its samples (identical in all its lanes)
   float acc_s = 0.0f, acc_rx = 0.0f, acc_ry = 0.0f, acc_bx = 0.0f, acc_by = 0.0f;
@@ -530,14 +526,10 @@ __device__ __forceinline__ void bwd_sample_body(const Params &p, int block, int 
       const int pt = pc0 + pp;
       const int l = (int)small_div((uint32_t)pt, kmg);
       const int64_t gi = pr(gg) * p.LK + pt;
-      const float2 v = *reinterpret_cast<const float2 *>(p.loc + 2 * gi);
-      const float z = p.attn[gi];
-      float2 xy = v;
-      float A = z;
+      const float2 xy = *reinterpret_cast<const float2 *>(p.loc + 2 * gi);
+      const float A = p.attn[gi];
       if constexpr (FUSE) {
-        xy = form_loc<true>(p, v, l, load_ref(p, pqry[gg]), sH, sW);
-        A = p.seg_softmax ? segment_softmax(z, p.LK) : softmax_weight(z, sst[gg]);
-        soff[pp * dstride + gg] = v;
+        if (p.ref_dim == 4) soff[pp * dstride + gg] = *reinterpret_cast<const float2 *>(p.offsets + 2 * gi);
       }
       // the weight itself, in the map or not (the softmax gradient needs it;
       // corners outside the map drop the scatter's atomics)
@@ -590,15 +582,7 @@ __device__ __forceinline__ void bwd_sample_body(const Params &p, int block, int 
         gx = group_sum<LPP>(gx, lpp);
         gy = group_sum<LPP>(gy, lpp);
         const float glx = d.aw * gx, gly = d.ah * gy;
-        float3 r = make_float3(ga, glx, gly);
-        if constexpr (FUSE) {
-          const float A = sA[pp * dstride + g];
-          // reference points: d loc / d offset = 1 / size cancels the size in
-          // grad_loc, so the offset gradient is A * d sample / d x itself (zero
-          // for a sample outside the map, as grad_loc is)
-          if (p.ref_dim == 2) r = make_float3(ga, d.aw != 0.0f ? A * gx : 0.0f, d.ah != 0.0f ? A * gy : 0.0f);
-        }
-        if (j == 0) res[pp * dstride + g] = r;
+        if (j == 0) res[pp * dstride + g] = make_float3(ga, glx, gly);
         if constexpr (FUSE) {
           acc_s = fmaf(sA[pp * dstride + g], ga, acc_s);
           acc_rx += glx;
@@ -629,6 +613,9 @@ __device__ __forceinline__ void bwd_sample_body(const Params &p, int block, int 
         if (p.ref_dim == 4) {
           const float4 rf = load_ref(p, pqry[gg]);
           gl = make_float2(r.y * rf.z, r.z * rf.w);
+        } else {
+          const int l = (int)small_div((uint32_t)(pc0 + pp), kmg);
+          gl = make_float2(r.y / (float)sW[l], r.z / (float)sH[l]);
         }
       }
       p.grad_attn[gi] = gz;
@@ -647,8 +634,7 @@ __device__ __forceinline__ void bwd_sample_body(const Params &p, int block, int 
       for (int i = tid; i < npairs * p.LK; i += kBlock) {
         const int gg = i / p.LK;
         const int64_t gi = pr(gg) * p.LK + (i - gg * p.LK);
-        const float A = softmax_weight(p.attn[gi], sst[gg]);
-        p.grad_attn[gi] = A * (p.grad_attn[gi] - ssum[gg]);
+        p.grad_attn[gi] = p.attn[gi] * (p.grad_attn[gi] - ssum[gg]);
       }
     }
   }
@@ -658,6 +644,53 @@ template <typename T, int VEC, int NCG, int LPP, bool FUSE>
 __global__ __launch_bounds__(kBlock) void bwd_sample_kernel(const Params p) {
   __shared__ __align__(16) unsigned char smem[sample_smem<FUSE>()];
   bwd_sample_body<T, VEC, NCG, LPP, FUSE>(p, blockIdx.x, gridDim.x, smem);
+}
+
+// ------------------------------------------- fused inputs for the backward
+//
+// The backward with fused inputs first forms every sample's location and
+// weight once (the same arithmetic as the fused forward) into the workspace;
+// the binning passes and the sample pass then read them as plain inputs. With
+// a power-of-two L*K up to 64, thread s takes sample s and a pair's samples
+// are consecutive lanes (softmax from lane exchanges); otherwise thread P
+// takes pair P and walks its L*K logits.
+__global__ __launch_bounds__(kBlock) void fused_inputs_kernel(const Params p, float *loc_out, float *attn_out) {
+  __shared__ int32_t sH[kMaxLevels], sW[kMaxLevels], sS[kMaxLevels];
+  load_levels(p, sH, sW, sS);
+  __syncthreads();
+  const uint32_t LK = (uint32_t)p.LK, K = (uint32_t)p.K;
+  if (p.seg_softmax) {
+    // samples of one launch have 32-bit indices; L*K is a power of two here
+    const uint32_t total = (uint32_t)(p.pairs * p.LK);
+    const uint32_t s = blockIdx.x * (uint32_t)kBlock + threadIdx.x;
+    const bool ok = s < total;  // whole pairs drop out together
+    const uint32_t P = (ok ? s : 0u) >> (31 - __builtin_clz(LK));
+    const uint32_t pt = (ok ? s : 0u) & (LK - 1u);
+    const int l = (int)small_div(pt, small_magic(K));
+    const float2 v = ok ? *reinterpret_cast<const float2 *>(p.offsets + 2 * (size_t)s) : make_float2(0.0f, 0.0f);
+    const float z = ok ? p.logits[s] : 0.0f;
+    const float A = segment_softmax(z, p.LK);
+    if (!ok) return;
+    const float2 xy = form_loc<true>(p, v, l, load_ref(p, P / (uint32_t)p.M), sH, sW);
+    *reinterpret_cast<float2 *>(loc_out + 2 * (size_t)s) = xy;
+    attn_out[s] = A;
+    return;
+  }
+  const int64_t P = (int64_t)blockIdx.x * kBlock + threadIdx.x;
+  if (P >= p.pairs) return;
+  const float *z = p.logits + P * p.LK;
+  float mx = -INFINITY;
+  for (int i = 0; i < p.LK; ++i) mx = fmaxf(mx, z[i]);
+  float sum = 0.0f;
+  for (int i = 0; i < p.LK; ++i) sum += expf(z[i] - mx);
+  const float2 st = make_float2(mx, 1.0f / sum);
+  const float4 rf = load_ref(p, (uint32_t)(P / p.M));
+  for (int i = 0; i < p.LK; ++i) {
+    const int64_t s = P * p.LK + i;
+    const float2 v = *reinterpret_cast<const float2 *>(p.offsets + 2 * s);
+    *reinterpret_cast<float2 *>(loc_out + 2 * s) = form_loc<true>(p, v, (int)((uint32_t)i / K), rf, sH, sW);
+    attn_out[s] = softmax_weight(z[i], st);
+  }
 }
 
 // ------------------------------------------------------ tile binning (sort)
@@ -714,13 +747,10 @@ __device__ __forceinline__ void zero_split_body(const Params &p, int block, int 
                                                 const int32_t *sW, const int32_t *sS, const int32_t *sTW,
                                                 const int32_t *sToff);
 
-template <int MODE, bool FUSE>
+template <int MODE>
 __global__ __launch_bounds__(kBlock) void bin_kernel(const Params p) {
   __shared__ uint32_t cnt[kBinCap];
   __shared__ uint32_t gbase[MODE == 1 ? kBinCap : 1];
-  // softmax statistics of the block's pairs when L*K is not a power of two:
-  // then L*K >= 3, so a block holds at most 1024 / 3 pairs
-  __shared__ float2 bst[MODE == 1 && FUSE ? 1024 / 3 + 1 : 1];
   __shared__ int32_t sH[kMaxLevels], sW[kMaxLevels], sS[kMaxLevels], sTW[kMaxLevels], sToff[kMaxLevels];
   load_tile_levels(p, sH, sW, sS, sTW, sToff);
   const int tid = threadIdx.x;
@@ -746,25 +776,6 @@ __global__ __launch_bounds__(kBlock) void bin_kernel(const Params p) {
   uint4 *rec_out = reinterpret_cast<uint4 *>(p.ws.entries);
   if (local)
     for (int i = tid; i < p.TPI; i += kBlock) cnt[i] = 0;
-  // Weights from logits (fused inputs): a pair's L*K samples are consecutive
-  // lanes here, so a power-of-two L*K up to 64 takes its softmax from lane
-  // exchanges; otherwise the block's pairs get their statistics first, ls
-  // lanes per pair.
-  const bool seg = (p.LK & (p.LK - 1)) == 0 && p.LK <= 64;
-  if constexpr (FUSE && MODE == 1) {
-    if (!seg) {
-      const int nq = nsamp / p.LK;
-      int ls = 1;
-      while (ls < 64 && 2 * ls * nq <= kBlock) ls *= 2;
-      for (int base = 0; base < nq; base += kBlock / ls) {
-        const int qi = base + tid / ls;
-        const bool act = qi < nq;
-        const int64_t P = ((int64_t)n * p.Lq + q0 + (act ? qi : 0)) * p.M + m;
-        const float2 st = pair_softmax_stats<0>(p.attn + P * p.LK, act, tid % ls, ls, p.LK);
-        if (act && tid % ls == 0) bst[qi] = st;
-      }
-    }
-  }
   __syncthreads();
 
   // The thread's four samples: all their loads first (one round trip), then
@@ -797,13 +808,8 @@ __global__ __launch_bounds__(kBlock) void bin_kernel(const Params p) {
     const int pt = i - qi * p.LK;
     const uint32_t P = (uint32_t)(((int64_t)n * p.Lq + q0 + qi) * p.M + m);
     const int l = (int)small_div((uint32_t)pt, kmg);
-    float2 xy = xyv[r];
-    if constexpr (FUSE) xy = form_loc<true>(p, xy, l, load_ref(p, (uint32_t)(n * p.Lq + q0 + qi)), sH, sW);
-    float A = av[r];
-    if constexpr (MODE == 1 && FUSE) {
-      // before the branch below: every lane of the pair takes part
-      A = seg ? segment_softmax(A, p.LK) : softmax_weight(A, bst[qi]);
-    }
+    const float2 xy = xyv[r];
+    const float A = av[r];
     Footprint f;
     if (!sample_footprint(xy.x, xy.y, sH[l], sW[l], f)) continue;
     if (MODE == 1) rec[r] = make_uint4(P, __float_as_uint(f.x), __float_as_uint(f.y), __float_as_uint(A));
@@ -1322,7 +1328,7 @@ void fill_tiles(LevelTable &lv, const int64_t *spatial_shapes, int64_t L, int32_
 }
 
 WorkspaceLayout workspace_layout(const int64_t *spatial_shapes, int64_t L, int64_t nimg, int64_t M, int64_t Lq,
-                                 int64_t K) {
+                                 int64_t K, bool fused) {
   int64_t tpi = 0;
   for (int64_t l = 0; l < L; ++l)
     tpi += ((spatial_shapes[2 * l] + kTile - 1) / kTile) * ((spatial_shapes[2 * l + 1] + kTile - 1) / kTile);
@@ -1340,8 +1346,11 @@ WorkspaceLayout workspace_layout(const int64_t *spatial_shapes, int64_t L, int64
   w.off_nwork = o;   o = up(o + 4);
   w.off_split = o;   o = up(o + 4 * (size_t)w.T);
   w.off_entries = o; o = up(o + 16 * (size_t)w.Emax);
-  // fused inputs: reference-gradient sums per pair
-  w.off_refpart = o; o = up(o + 16 * (size_t)(nimg * Lq * M));
+  // fused inputs: reference-gradient sums per pair, the formed locations and
+  // weights per sample
+  w.off_refpart = o; o = up(o + (fused ? 16 * (size_t)(nimg * Lq * M) : 0));
+  w.off_floc = o;    o = up(o + (fused ? 8 * (size_t)(nimg * Lq * M * L * K) : 0));
+  w.off_fattn = o;   o = up(o + (fused ? 4 * (size_t)(nimg * Lq * M * L * K) : 0));
   w.bytes = o;
   return w;
 }
@@ -1357,6 +1366,22 @@ hipError_t launch_backward(const Params &p_in, DType dt, const LaunchShape &s, h
   set_sample_shape(p, s, true);
   const bool fuse = p.ref_dim != 0;
   hipError_t e;
+  // 0. fused inputs: every sample's location and weight, formed once into
+  //    the workspace, are the loc and attn of the passes below
+  if (fuse) {
+    Params q = p;
+    q.seg_softmax = (p.LK & (p.LK - 1)) == 0 && p.LK <= 64 ? 1 : 0;
+    const int64_t items = q.seg_softmax ? p.pairs * p.LK : p.pairs;
+    float *lo = p.ws.floc, *ao = p.ws.fattn;
+    void *args[] = {&q, &lo, &ao};
+    const int64_t blocks = (items + kBlock - 1) / kBlock;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    e = hipLaunchKernel(reinterpret_cast<const void *>(fused_inputs_kernel), dim3((unsigned)blocks), dim3(kBlock),
+                        args, 0, stream);
+    if (e != hipSuccess) return e;
+    p.loc = p.ws.floc;
+    p.attn = p.ws.fattn;
+  }
   // Sparse launches (few samples per 8x8 value tile, e.g. decoder queries): a
   // tile sort would cost more than it saves; grad_value is zero-filled and
   // the sample pass adds each corner's contribution with float atomics.
@@ -1380,10 +1405,8 @@ hipError_t launch_backward(const Params &p_in, DType dt, const LaunchShape &s, h
     //    the tiles whose grad_value is summed over several work items
     const int64_t bin_blocks = (int64_t)p.N * p.M * ((p.Lq + p.qpb - 1) / p.qpb);
     const int64_t bin0_blocks = (int64_t)p.N * p.M * ((p.Lq + p.qpb0 - 1) / p.qpb0);
-    const void *bin0 = fuse ? reinterpret_cast<const void *>(bin_kernel<0, true>)
-                            : reinterpret_cast<const void *>(bin_kernel<0, false>);
-    const void *bin1 = fuse ? reinterpret_cast<const void *>(bin_kernel<1, true>)
-                            : reinterpret_cast<const void *>(bin_kernel<1, false>);
+    const void *bin0 = reinterpret_cast<const void *>(bin_kernel<0>);
+    const void *bin1 = reinterpret_cast<const void *>(bin_kernel<1>);
     if ((e = launch_fn(bin0, bin0_blocks, kBlock, 1, p, stream)) != hipSuccess) return e;
     if ((e = launch_fn(reinterpret_cast<const void *>(scan_kernel), 1, 1024, 1, p, stream)) != hipSuccess) return e;
     if ((e = launch_fn(bin1, bin_blocks + 256, kBlock, 1, p, stream)) != hipSuccess) return e;
