@@ -862,54 +862,61 @@ __global__ __launch_bounds__(kBlock) void bin_kernel(const Params p) {
 // Exclusive scan of the tile counts (one workgroup of 1024 threads, each
 // owning a run of consecutive tiles) and the list of grad_value work items:
 // a tile gives ceil(count / kPartEntries) items, at least one (an empty tile's
-// item writes its zeros). Tiles with several items are listed so that they can
-// be zeroed first.
+// item writes its zeros). Tiles with several items are listed, in tile order
+// (a third prefix sum gives each its slot), so that they can be zeroed first.
 __global__ __launch_bounds__(1024) void scan_kernel(const Params p) {
-  __shared__ uint32_t wsum_c[16], wsum_p[16];
+  __shared__ uint32_t wsum_c[16], wsum_p[16], wsum_s[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int per = (p.T + 1023) / 1024;
   const int t0 = tid * per, t1 = min(p.T, t0 + per);
   auto parts_of = [&](uint32_t c) -> uint32_t {
     return max(1u, (c + kPartEntries - 1) / kPartEntries);
   };
-  uint32_t rc = 0, rp = 0;
+  // per thread: entries, work items and split tiles of its run
+  uint32_t rc = 0, rp = 0, rs = 0;
   for (int t = t0; t < t1; ++t) {
     const uint32_t c = p.ws.tile_count[t];
+    const uint32_t parts = parts_of(c);
     rc += c;
-    rp += parts_of(c);
+    rp += parts;
+    rs += parts > 1 ? 1u : 0u;
   }
-  uint32_t ic = rc, ip = rp;
+  uint32_t ic = rc, ip = rp, is = rs;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t yc = __shfl_up(ic, o), yp = __shfl_up(ip, o);
+    const uint32_t yc = __shfl_up(ic, o), yp = __shfl_up(ip, o), ys = __shfl_up(is, o);
     if (lane >= o) {
       ic += yc;
       ip += yp;
+      is += ys;
     }
   }
   if (lane == 63) {
     wsum_c[wave] = ic;
     wsum_p[wave] = ip;
+    wsum_s[wave] = is;
   }
   __syncthreads();
-  uint32_t oc = 0, op = 0, tc = 0, tp = 0;
+  uint32_t oc = 0, op = 0, os = 0, tc = 0, tp = 0, ts = 0;
 #pragma unroll
   for (int w = 0; w < 16; ++w) {
     if (w < wave) {
       oc += wsum_c[w];
       op += wsum_p[w];
+      os += wsum_s[w];
     }
     tc += wsum_c[w];
     tp += wsum_p[w];
+    ts += wsum_s[w];
   }
-  uint32_t start = oc + ic - rc, wb = op + ip - rp;
+  uint32_t start = oc + ic - rc, wb = op + ip - rp, sb = os + is - rs;
   uint4 *items = reinterpret_cast<uint4 *>(p.ws.work_item);
   for (int t = t0; t < t1; ++t) {
     const uint32_t c = p.ws.tile_count[t];
     const uint32_t parts = parts_of(c);
     p.ws.tile_start[t] = start;
     p.ws.tile_cursor[t] = start;
-    if (parts > 1) p.ws.split_list[atomicAdd(p.ws.tile_count + p.T, 1u)] = (uint32_t)t;
+    if (parts > 1) p.ws.split_list[sb++] = (uint32_t)t;
     // Items are stored last tile first: each (head, image) block of tiles
     // ends with the coarse levels, whose crowded tiles then start first.
     for (uint32_t k = 0; k < parts; ++k) {
@@ -922,6 +929,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(const Params p) {
   }
   if (tid == 0) {
     p.ws.tile_start[p.T] = tc;
+    p.ws.tile_count[p.T] = ts;  // number of split tiles
     *p.ws.n_work = tp;
   }
 }
@@ -967,6 +975,48 @@ __device__ __forceinline__ void zero_split_body(const Params &p, int block, int 
 // its pixel's contributions to CS channels in registers, reading the grad_out
 // row slices straight from memory with several loads in flight.
 constexpr size_t kGvSmem = 4 * kPartEntries * sizeof(uint2) + (2 * kTilePix + 1) * 4 + 5 * kMaxLevels * 4;
+
+// Sums w * grad_out[pair, channels] over the list entries [jb, je) of one
+// pixel into acc, U entries in flight. VECP: 16-byte loads of interleaved
+// pieces (channel c0 + (c / VG) * 4 * VG + c % VG, the four threads of a pixel
+// covering whole 64-byte segments); otherwise element loads of the cnum
+// channels from c0 on. Rows of absent slots (and channels past cnum) read past
+// the buffer, which returns zeros; their weight is 0 too.
+template <typename T, int CS, bool VECP>
+__device__ __forceinline__ void gv_accumulate(const uint2 *lst, uint32_t jb, uint32_t je,
+                                              __amdgpu_buffer_rsrc_t ro, uint32_t D, uint32_t c0, int cnum,
+                                              float (&acc)[CS]) {
+  constexpr int VG = 16 / T::size;
+  constexpr int U = 4;
+  for (uint32_t j = jb; j < je; j += U) {
+    float g[U][CS];
+    float w[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      // read unconditionally (slots past je read the LDS words that follow
+      // the list, which the workgroup owns) so the reads issue together
+      const bool ok = j + u < je;
+      const uint2 r2 = lst[j + u];
+      w[u] = ok ? __uint_as_float(r2.y) : 0.0f;
+      const uint32_t base = ok ? r2.x * D + c0 : kOobElem;
+      if constexpr (VECP) {
+#pragma unroll
+        for (int q = 0; q < CS / VG; ++q)
+          load_vals<T, VG>(ro, (base + (uint32_t)(q * 4 * VG)) * (uint32_t)T::size,
+                           *reinterpret_cast<float(*)[VG]>(&g[u][q * VG]));
+      } else {
+#pragma unroll
+        for (int c = 0; c < CS; ++c)
+          load_vals<T, 1>(ro, (c < cnum ? base + (uint32_t)c : kOobElem) * (uint32_t)T::size,
+                          *reinterpret_cast<float(*)[1]>(&g[u][c]));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int c = 0; c < CS; ++c) acc[c] = fmaf(w[u], g[u][c], acc[c]);
+  }
+}
 
 template <typename T, int CS>
 __device__ __forceinline__ void gv_body(const Params &p, uint32_t bx, int cgroup, unsigned char *smem) {
@@ -1059,36 +1109,14 @@ __device__ __forceinline__ void gv_body(const Params &p, uint32_t bx, int cgroup
 #pragma unroll
   for (int c = 0; c < CS; ++c) acc[c] = 0.0f;
   const uint32_t jb = off[pix], je = off[pix + 1];
-  constexpr int U = 4;  // list entries in flight per thread
-  for (uint32_t j = jb; j < je; j += U) {
-    float g[U][CS];
-    float w[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const bool ok = j + u < je;
-      const uint2 r2 = ok ? lst[j + u] : make_uint2(0, 0);
-      w[u] = __uint_as_float(r2.y);
-      // rows of absent slots read past the buffer (zeros); weight is 0 too
-      const uint32_t base = ok ? r2.x * (uint32_t)p.D + (uint32_t)cbeg : kOobElem;
-      if constexpr (CS >= VG) {
-        if (vec) {
-          const uint32_t vbase = ok ? r2.x * (uint32_t)p.D + (uint32_t)(c0 + slice * VG) : kOobElem;
-#pragma unroll
-          for (int q = 0; q < CS / VG; ++q)
-            load_vals<T, VG>(ro, (vbase + (uint32_t)(q * 4 * VG)) * (uint32_t)T::size,
-                             *reinterpret_cast<float(*)[VG]>(&g[u][q * VG]));
-          continue;
-        }
-      }
-#pragma unroll
-      for (int c = 0; c < CS; ++c)
-        load_vals<T, 1>(ro, (c < cnum ? base + (uint32_t)c : kOobElem) * (uint32_t)T::size,
-                        *reinterpret_cast<float(*)[1]>(&g[u][c]));
+  if constexpr (CS >= VG) {
+    if (vec) {
+      gv_accumulate<T, CS, true>(lst, jb, je, ro, (uint32_t)p.D, (uint32_t)(c0 + slice * VG), CS, acc);
+    } else {
+      gv_accumulate<T, CS, false>(lst, jb, je, ro, (uint32_t)p.D, (uint32_t)cbeg, cnum, acc);
     }
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int c = 0; c < CS; ++c) acc[c] = fmaf(w[u], g[u][c], acc[c]);
+  } else {
+    gv_accumulate<T, CS, false>(lst, jb, je, ro, (uint32_t)p.D, (uint32_t)cbeg, cnum, acc);
   }
 
   const int64_t row0 = (int64_t)n * p.S + sS[l];
