@@ -349,6 +349,80 @@ def grouped_passes(msda, torch, dev, steps, rotate, groups=(1, 2, 4)):
     return res
 
 
+def config_passes(msda, torch, dev, steps):
+    """The other configurations of the workload table, timed the same way
+    (HIP events around each call, buffer sets cycled so inputs come from HBM):
+    batched encoder forward in bf16 (N=8) and the encoder backward at N=2 with
+    K=4 and K=8. Algorithmic bytes: every input read once, every output
+    written once, value counted in full (every row is sampled)."""
+    import numpy as np
+
+    from workloads import config_workload
+
+    def dev_tensor(w, name):
+        if w.dtype == "bf16":
+            bits = getattr(w, name + "_bits")
+            return torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(getattr(w, name)).to(dev)
+
+    stream = torch.cuda.current_stream()
+    res = {}
+    for name, backward, rotate in (("batched_encoder_fwd_bf16", False, 2), ("encoder_bwd", True, 3),
+                                   ("encoder_bwd_k8", True, 2)):
+        w = config_workload(name)
+        d = w.dims
+        ss, ls = w.spatial_shapes, w.level_start
+        elem = 2 if w.dtype == "bf16" else 4
+        pts = w.points
+        vbytes = d["N"] * d["S"] * d["M"] * d["D"] * elem
+        obytes = d["N"] * d["Lq"] * d["M"] * d["D"] * elem
+        if backward:
+            alg = vbytes + obytes + 12 * pts + d["N"] * d["S"] * d["M"] * d["D"] * 4 + 12 * pts
+        else:
+            alg = vbytes + 12 * pts + obytes
+        sets = []
+        for _ in range(rotate):
+            s = {"value": dev_tensor(w, "value"), "loc": torch.from_numpy(w.loc).to(dev),
+                 "attn": torch.from_numpy(w.attn).to(dev)}
+            if backward:
+                s["g"] = dev_tensor(w, "grad_out")
+                s["gv"] = torch.empty(s["value"].shape, dtype=torch.float32, device=dev)
+                s["gl"] = torch.empty_like(s["loc"])
+                s["ga"] = torch.empty_like(s["attn"])
+                s["ws"] = torch.empty(msda.msda_backward_workspace_size(ss, ls, d["N"], d["S"], d["M"], d["D"],
+                                                                        d["L"], d["Lq"], d["K"]),
+                                      dtype=torch.uint8, device=dev)
+            else:
+                s["out"] = torch.empty((d["N"], d["Lq"], d["M"], d["D"]), dtype=s["value"].dtype, device=dev)
+            sets.append(s)
+
+        def run(s):
+            if backward:
+                msda.msda_backward(s["value"], ss, ls, s["loc"], s["attn"], s["g"], grad_value=s["gv"],
+                                   grad_loc=s["gl"], grad_attn=s["ga"], workspace=s["ws"])
+            else:
+                msda.msda_forward(s["value"], ss, ls, s["loc"], s["attn"], out=s["out"])
+
+        for i in range(3):
+            run(sets[i % rotate])
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for i in range(steps):
+            ev[i][0].record(stream)
+            run(sets[i % rotate])
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        ms = np.array([a.elapsed_time(b) for a, b in ev])
+        t = float(ms.mean()) * 1e-3
+        res[name] = {"workload": f"N={d['N']}, Lq={d['Lq']}, M={d['M']}, D={d['D']}, K={d['K']}, {w.dtype}, "
+                                 f"{'backward' if backward else 'forward'}",
+                     "us_mean": round(t * 1e6, 2), "us_median": round(float(np.median(ms)) * 1e3, 2),
+                     "points_per_s": pts / t, "alg_bytes": alg, "alg_GBps": round(alg / t / 1e9, 1),
+                     "hbm_frac": round(alg / t / 1e9 / HBM_PEAK_GBPS, 4)}
+        del sets
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -503,6 +577,7 @@ def main():
         result["decoder_latency"] = decoder_latency(msda, torch, dev)
         result["fused_inputs"] = fused_passes(msda, torch, dev, min(args.steps, 30), args.rotate)
         result["deformable_groups"] = grouped_passes(msda, torch, dev, min(args.steps, 20), args.rotate)
+        result["other_configs"] = config_passes(msda, torch, dev, min(args.steps, 20))
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
         result["cpu_baseline_pool"] = cpu_baseline_pool(w)

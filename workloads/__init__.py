@@ -49,12 +49,19 @@ def level_starts(shapes):
 
 
 def bf16_bits_from_f32(x):
-    """Round float32 to bfloat16 (round to nearest, ties to even); return uint16 bits."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    nan = np.isnan(np.asarray(x, dtype=np.float32))
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    bits = (rounded & 0xFFFF).astype(np.uint16)
-    bits[nan] = 0x7FC0
+    """Round float32 to bfloat16 (round to nearest, ties to even); return uint16 bits.
+
+    Works in uint32 in place: for every non-NaN pattern (at most 0xFF800000)
+    adding at most 0x8000 cannot wrap; NaN patterns are overwritten after."""
+    x32 = np.ascontiguousarray(x, dtype=np.float32)
+    u = x32.view(np.uint32)
+    t = u >> 16
+    t &= 1
+    t += 0x7FFF
+    t += u
+    t >>= 16
+    bits = t.astype(np.uint16)
+    bits[np.isnan(x32)] = 0x7FC0
     return bits
 
 
