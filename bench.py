@@ -440,8 +440,9 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build measures one GPU only; the sampling core needs no "
-                                   "collective and multi-GPU runs are not part of it",
+        print(json.dumps({"error": "the benchmark runs on one GPU only: the sampling core needs no "
+                                   "collective (batch or head sharding is exchange-free), so no "
+                                   "multi-GPU figure is measured",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 

@@ -72,7 +72,7 @@ typedef enum msda_dtype {
   MSDA_BF16 = 1  /* value / out / grad_out in bfloat16; arithmetic in float32 */
 } msda_dtype;
 
-/* Limits of this build. */
+/* Limits of the library. */
 #define MSDA_MAX_LEVELS 16
 #define MSDA_MAX_POINTS 16
 #define MSDA_MAX_CHANNELS 1024

@@ -295,7 +295,7 @@ const char *msda_status_string(msda_status status) {
   switch (status) {
     case MSDA_SUCCESS: return "MSDA_SUCCESS: no error";
     case MSDA_ERROR_INVALID_VALUE: return "MSDA_ERROR_INVALID_VALUE: null pointer, bad size or level outside S";
-    case MSDA_ERROR_NOT_SUPPORTED: return "MSDA_ERROR_NOT_SUPPORTED: shape, size or dtype beyond this build's limits";
+    case MSDA_ERROR_NOT_SUPPORTED: return "MSDA_ERROR_NOT_SUPPORTED: shape, size or dtype beyond the library's limits";
     case MSDA_ERROR_MISALIGNED: return "MSDA_ERROR_MISALIGNED: a device pointer is not aligned to its element size";
     case MSDA_ERROR_LAUNCH: return "MSDA_ERROR_LAUNCH: a kernel launch failed";
     case MSDA_ERROR_WORKSPACE: return "MSDA_ERROR_WORKSPACE: workspace missing or smaller than msda_backward_workspace_size";
