@@ -204,3 +204,27 @@ def test_binding_rejects_host_tensors():
     attn = torch.zeros(1, 1, 1, 1, 1)
     with pytest.raises(ValueError, match="device tensor"):
         msda.msda_forward(x, [[2, 2]], [0], loc, attn)
+
+
+def test_header_compiles_as_c_and_links(tmp_path):
+    """A plain C11 program (tests/c/abi_host.c) includes the header, links the
+    library and runs its host-side paths: validation, status strings,
+    workspace size and the checks made before any HIP call."""
+    import shutil
+    import subprocess
+
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    rocm_inc = os.path.join(os.environ.get("ROCM_PATH", "/opt/rocm"), "include")
+    lib_dir = os.path.dirname(binding.LIB_PATH)
+    exe = str(tmp_path / "abi_host")
+    cmd = [cc, "-std=c11", "-Wall", "-Wextra", "-pedantic", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", os.path.join(ROOT, "include"), "-isystem", rocm_inc,
+           os.path.join(ROOT, "tests", "c", "abi_host.c"), "-o", exe,
+           "-L", lib_dir, "-lmsda", "-Wl,-rpath," + lib_dir]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+    run = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert run.returncode == 0, run.stdout + run.stderr
+    assert run.stdout.strip().endswith("OK")
