@@ -1028,7 +1028,13 @@ __device__ __forceinline__ void gv_accumulate(const uint2 *lst, uint32_t jb, uin
                                               __amdgpu_buffer_rsrc_t ro, uint32_t D, uint32_t c0, int cnum,
                                               float (&acc)[CS]) {
   constexpr int VG = 16 / T::size;
-  constexpr int U = 4;
+  // entries in flight per thread (measured: 8 beats 4 up to 8 channels per
+  // thread, most for bf16 rows, one 16-byte load per entry; with 16 channels
+  // 8 entries cost occupancy); slots past je read at most 56 bytes beyond the
+  // list, inside the tile counters that follow it in LDS
+  constexpr int U = CS >= 16 ? 4 : 8;
+  static_assert((U - 1) * sizeof(uint2) <= kTilePix * sizeof(uint32_t),
+                "the list over-read must stay inside the tile counters");
   for (uint32_t j = jb; j < je; j += U) {
     float g[U][CS];
     float w[U];
