@@ -782,7 +782,7 @@ constexpr int kBinCap = 2048;      // LDS tile counters of one (image, head)
 // 16-byte records {pair, x, y, attn} (x, y: the sample's index-space
 // coordinate), so the grad_value pass needs no access to loc or attn.
 // Workgroup b covers image n, head m and queries [q0, q0 + qpb); its samples
-// are the (q, l, k) of that range, at most 4 per thread. Tiles are numbered
+// are the (q, l, k) of that range, at most 8 per thread. Tiles are numbered
 // head-major: ((m * N + n) * TPI) + tile within the (image, head).
 __device__ __forceinline__ void zero_split_body(const Params &p, int block, int nblocks, const int32_t *sH,
                                                 const int32_t *sW, const int32_t *sS, const int32_t *sTW,
@@ -795,9 +795,10 @@ __global__ __launch_bounds__(kBlock) void bin_kernel(const Params p) {
   __shared__ int32_t sH[kMaxLevels], sW[kMaxLevels], sS[kMaxLevels], sTW[kMaxLevels], sToff[kMaxLevels];
   load_tile_levels(p, sH, sW, sS, sTW, sToff);
   const int tid = threadIdx.x;
-  // the counting pass takes 8 samples per thread (it keeps no per-sample
-  // state), the scatter pass 4
-  constexpr int NS = MODE == 0 ? 8 : 4;
+  // 8 samples per thread in both passes (measured for the scatter pass: 8
+  // beat 4 and 2 despite its register count; the longer per-tile runs also
+  // help the grad_value pass)
+  constexpr int NS = 8;
   const int qpb = MODE == 0 ? p.qpb0 : p.qpb;
   const int qblocks = (p.Lq + qpb - 1) / qpb;
   const int bin_blocks = p.N * p.M * qblocks;
@@ -819,7 +820,7 @@ __global__ __launch_bounds__(kBlock) void bin_kernel(const Params p) {
     for (int i = tid; i < p.TPI; i += kBlock) cnt[i] = 0;
   __syncthreads();
 
-  // The thread's four samples: all their loads first (one round trip), then
+  // The thread's samples: all their loads first (one round trip), then
   // the tile walk. Sample i is (query qi = i / LK, point pt = i % LK).
   const uint32_t lkmg = small_magic((uint32_t)p.LK), kmg = small_magic((uint32_t)p.K);
   float2 xyv[NS];
@@ -1436,7 +1437,7 @@ hipError_t launch_forward(const Params &p, DType dt, const LaunchShape &s, hipSt
 
 hipError_t launch_backward(const Params &p_in, DType dt, const LaunchShape &s, hipStream_t stream) {
   Params p = p_in;
-  p.qpb = max(1, 1024 / p.LK);
+  p.qpb = max(1, 2048 / p.LK);
   p.qpb0 = max(1, 2048 / p.LK);
   set_sample_shape(p, s, true);
   const bool fuse = p.ref_dim != 0;
