@@ -156,7 +156,8 @@ def test_encoder_backward_full_size_sampled(name):
 # ------------------------------------------------------------------------ edge cases
 
 @pytest.mark.parametrize("D,dtype", [(5, "f32"), (12, "f32"), (64, "f32"), (100, "f32"),
-                                     (1024, "f32"), (6, "bf16"), (8, "bf16"), (40, "bf16")])
+                                     (1024, "f32"), (6, "bf16"), (8, "bf16"), (40, "bf16"),
+                                     (1024, "bf16")])
 def test_channel_counts(D, dtype):
     w = uniform_workload(N=2, shapes=((7, 9), (4, 5)), Lq=19, M=3, D=D, K=3, dtype=dtype,
                          seed=100 + D, with_grad=True)
@@ -179,6 +180,28 @@ def test_max_levels_and_points():
     w = uniform_workload(N=1, shapes=shapes, Lq=9, M=2, D=8, K=16, seed=200, with_grad=True)
     note("L=16 K=16 (several descriptor chunks per workgroup)")
     assert_f32("out", to_f64(gpu_forward(w)), msda_forward(*_oracle_args(w)))
+    gv, gl, ga = (to_f64(t) for t in gpu_backward(w))
+    rgv, rgl, rga = msda_backward(*_oracle_args(w), w.grad_out)
+    assert_f32("grad_value", gv, rgv)
+    assert_f32("grad_attn", ga, rga)
+    assert_grad_loc(gl, rgl, w.spatial_shapes)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_hot_shapes_with_odd_point_counts(dtype):
+    """D=32 with 16-byte lanes and enough pairs (40000) for the launch shapes
+    that batch several samples' corner loads per lane (three in the bf16
+    forward, two in the backward's sample pass), with L*K = 9 samples per
+    head, so the last batch of every chunk is partly empty."""
+    w = uniform_workload(N=1, shapes=((24, 40), (12, 20), (6, 10)), Lq=5000, M=8, D=32, K=3,
+                         dtype=dtype, seed=300, with_grad=True)
+    note(f"hot launch shapes with L*K=9, {dtype}, 40000 pairs")
+    out = to_f64(gpu_forward(w))
+    ref = msda_forward(*_oracle_args(w))
+    if dtype == "f32":
+        assert_f32("out", out, ref)
+    else:
+        _check_bf16_out(out, ref)
     gv, gl, ga = (to_f64(t) for t in gpu_backward(w))
     rgv, rgl, rga = msda_backward(*_oracle_args(w), w.grad_out)
     assert_f32("grad_value", gv, rgv)
