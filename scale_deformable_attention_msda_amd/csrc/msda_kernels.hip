@@ -907,72 +907,86 @@ __global__ __launch_bounds__(kBlock) void bin_kernel(const Params p) {
 // item writes its zeros). Tiles with several items are listed, in tile order
 // (a third prefix sum gives each its slot), so that they can be zeroed first.
 __global__ __launch_bounds__(1024) void scan_kernel(const Params p) {
-  __shared__ uint32_t wsum_c[16], wsum_p[16], wsum_s[16];
+  __shared__ uint32_t wsum_c[16], wsum_q[16], wsum_s[16], wsum_u[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int per = (p.T + 1023) / 1024;
   const int t0 = tid * per, t1 = min(p.T, t0 + per);
   auto parts_of = [&](uint32_t c) -> uint32_t {
     return max(1u, (c + kPartEntries - 1) / kPartEntries);
   };
-  // per thread: entries, work items and split tiles of its run
-  uint32_t rc = 0, rp = 0, rs = 0;
+  // per thread, over its run of tiles: entries, work items of split tiles,
+  // split tiles, single-item tiles
+  uint32_t rc = 0, rq = 0, rs = 0, ru = 0;
   for (int t = t0; t < t1; ++t) {
     const uint32_t c = p.ws.tile_count[t];
     const uint32_t parts = parts_of(c);
     rc += c;
-    rp += parts;
-    rs += parts > 1 ? 1u : 0u;
+    if (parts > 1) {
+      rq += parts;
+      ++rs;
+    } else {
+      ++ru;
+    }
   }
-  uint32_t ic = rc, ip = rp, is = rs;
+  uint32_t ic = rc, iq = rq, is = rs, iu = ru;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t yc = __shfl_up(ic, o), yp = __shfl_up(ip, o), ys = __shfl_up(is, o);
+    const uint32_t yc = __shfl_up(ic, o), yq = __shfl_up(iq, o), ys = __shfl_up(is, o), yu = __shfl_up(iu, o);
     if (lane >= o) {
       ic += yc;
-      ip += yp;
+      iq += yq;
       is += ys;
+      iu += yu;
     }
   }
   if (lane == 63) {
     wsum_c[wave] = ic;
-    wsum_p[wave] = ip;
+    wsum_q[wave] = iq;
     wsum_s[wave] = is;
+    wsum_u[wave] = iu;
   }
   __syncthreads();
-  uint32_t oc = 0, op = 0, os = 0, tc = 0, tp = 0, ts = 0;
+  uint32_t oc = 0, oq = 0, os = 0, ou = 0, tc = 0, tq = 0, ts = 0, tu = 0;
 #pragma unroll
   for (int w = 0; w < 16; ++w) {
     if (w < wave) {
       oc += wsum_c[w];
-      op += wsum_p[w];
+      oq += wsum_q[w];
       os += wsum_s[w];
+      ou += wsum_u[w];
     }
     tc += wsum_c[w];
-    tp += wsum_p[w];
+    tq += wsum_q[w];
     ts += wsum_s[w];
+    tu += wsum_u[w];
   }
-  uint32_t start = oc + ic - rc, wb = op + ip - rp, sb = os + is - rs;
+  uint32_t start = oc + ic - rc, qb = oq + iq - rq, sb = os + is - rs, ub = ou + iu - ru;
   uint4 *items = reinterpret_cast<uint4 *>(p.ws.work_item);
+  // Work items: every split tile's items first (the longest work starts
+  // first), coarse levels first (tiles in reverse order), then one item per
+  // remaining tile, also in reverse tile order.
   for (int t = t0; t < t1; ++t) {
     const uint32_t c = p.ws.tile_count[t];
     const uint32_t parts = parts_of(c);
     p.ws.tile_start[t] = start;
     p.ws.tile_cursor[t] = start;
-    if (parts > 1) p.ws.split_list[sb++] = (uint32_t)t;
-    // Items are stored last tile first: each (head, image) block of tiles
-    // ends with the coarse levels, whose crowded tiles then start first.
-    for (uint32_t k = 0; k < parts; ++k) {
-      const uint32_t e0 = start + k * kPartEntries;
-      items[tp - 1 - (wb + k)] = make_uint4((uint32_t)t, e0, min(e0 + (uint32_t)kPartEntries, start + c),
-                                            parts > 1 ? 1u : 0u);
+    if (parts > 1) {
+      p.ws.split_list[sb++] = (uint32_t)t;
+      for (uint32_t k = 0; k < parts; ++k) {
+        const uint32_t e0 = start + k * kPartEntries;
+        items[tq - 1 - (qb + k)] = make_uint4((uint32_t)t, e0, min(e0 + (uint32_t)kPartEntries, start + c), 1u);
+      }
+      qb += parts;
+    } else {
+      items[tq + tu - 1 - ub] = make_uint4((uint32_t)t, start, start + c, 0u);
+      ++ub;
     }
     start += c;
-    wb += parts;
   }
   if (tid == 0) {
     p.ws.tile_start[p.T] = tc;
     p.ws.tile_count[p.T] = ts;  // number of split tiles
-    *p.ws.n_work = tp;
+    *p.ws.n_work = tq + tu;
   }
 }
 
