@@ -14,7 +14,7 @@
 //     so every corner read of a pair is one coalesced segment.
 //   * Per workgroup, each sample's coordinate transform, corner offsets and
 //     corner weights are computed once (one lane per sample, reading loc and
-//     attn coalesced) and staged in LDS as a 32/48-byte descriptor; every lane
+//     attn coalesced) and staged in LDS as a 32-byte descriptor; every lane
 //     of the pair then reads the descriptor with an LDS broadcast.
 //   * Corners outside the map carry an offset past the buffer's num_records,
 //     so buffer loads return 0 and buffer atomics are dropped by the hardware:
@@ -24,7 +24,8 @@
 //   * Backward: per sample, the three dot products (grad_attn and the two
 //     location gradients) are reduced across the pair's lanes with DPP and
 //     written coalesced; grad_value is built per pixel tile from a counting
-//     sort of the samples (see the backward section).
+//     sort of the samples, or with float atomics when samples are sparse
+//     (see the backward section).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -312,6 +313,13 @@ struct __align__(16) FDesc {
   float w[4];       // attn * bilinear weight, 0 for corners outside the map
 };
 
+// Forward. A workgroup takes kBlock / lpp consecutive (n, q, m) pairs. For
+// each chunk of pc points: one thread per sample reads its location and
+// weight (with fused inputs: offset and logit, forming both), computes the
+// corner offsets and weights and writes the sample's descriptor to LDS; after
+// a barrier, the lanes of each pair walk its samples, gathering the four
+// corner rows and accumulating into registers. Finally each lane stores its
+// channels of out.
 template <typename T, int VEC, int NCG, int LPP, bool FUSE>
 __global__ __launch_bounds__(kBlock) void fwd_kernel(const Params p) {
   // bf16 rows: three samples' corner loads in flight per lane (measured
@@ -457,20 +465,31 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(const Params p) {
 // --------------------------------------------------------------- backward
 //
 // The backward runs as a short pipeline on the caller's stream:
-//   1. bwd_sample_kernel: grad_attn and grad_loc. Same gather as the forward;
-//      the three dot products of a sample are reduced across the pair's lanes.
+//   0. (fused inputs only) fused_inputs_kernel forms every sample's location
+//      and weight into the workspace; the passes below read them.
+//   Dense launches (many samples per value tile):
+//   1. zero_u32_kernel clears the tile counters.
 //   2. bin_kernel<count> / scan_kernel / bin_kernel<scatter>: a counting sort
 //      of (sample, 8x8-pixel tile) entries, one entry per tile that a sample's
 //      in-map corners touch. Workgroups own one (image, head) and a range of
 //      queries, so their tile histogram fits in LDS and only nonzero bins reach
-//      global memory (integer atomics, a few per workgroup).
-//   3. gv_kernel: one workgroup per tile (or per slice of a crowded tile). Its
-//      entries' corner contributions are bucketed by pixel in LDS, then each
-//      thread sums the contributions to the pixel it owns in registers and
-//      stores them. Float atomics appear only where a crowded tile is split.
+//      global memory (integer atomics, a few per workgroup). The scan lists
+//      the grad_value work items, crowded (split) tiles first; the scatter
+//      launch also clears those tiles.
+//   3. grad_value items and the sample gradients, in one launch for the hot
+//      shapes (bwd_fused_kernel: items first, then sample blocks) or as
+//      bwd_sample_kernel then gv_kernel. A grad_value item owns one tile (or a
+//      slice of a crowded one): its entries' corner contributions are
+//      bucketed by pixel in LDS, then each thread sums the contributions to
+//      the pixel it owns in registers and stores them; float atomics appear
+//      only for split tiles. The sample blocks compute grad_attn and grad_loc
+//      with the forward's gather, reducing each sample's three dot products
+//      across the pair's lanes.
+//   Sparse launches (decoder-sized): grad_value is zero-filled and the sample
+//   pass adds each corner's contribution with float atomics.
 // gfx950 float atomics (global and LDS) sustain a small fraction of the
-// integer LDS atomic and plain-store rates, so grad_value is never
-// accumulated with them in the common path.
+// integer LDS atomic and plain-store rates, so the dense path accumulates
+// grad_value without them.
 
 struct __align__(16) BDesc {
   uint32_t off[4];  // element offsets of the corners (kOobElem outside the map)
