@@ -28,6 +28,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, published
 KERNEL_SRC = os.path.join(ROOT, "scale_deformable_attention_msda_amd", "csrc", "msda_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "msda_encoder_fwd_bwd_hbm_traffic.md")
+TRACE_FILE = os.path.join(ROOT, "profiles", "msda_encoder_fwd_bwd_kernel_stats.md")
 
 
 def kernel_source_hash():
@@ -49,6 +50,26 @@ def measured_traffic():
         mm = re.search(rf"traffic_bytes_{key}:\s*([0-9.eE+]+)", text)
         if mm:
             out[key] = float(mm.group(1))
+    return out or None
+
+
+def traced_durations():
+    """Average pass durations (us) from the committed rocprofv3 kernel-trace
+    summary of this benchmark, if it was taken on the current kernel source:
+    the forward kernel, and the sum of the backward's kernels per call."""
+    if not os.path.exists(TRACE_FILE):
+        return None
+    text = open(TRACE_FILE).read()
+    m = re.search(r"Kernel source sha256 \(first 16 hex\): `([0-9a-f]+)`", text)
+    if not m or m.group(1) != kernel_source_hash():
+        return None
+    out = {}
+    mm = re.search(r"Forward \(fwd_kernel\) average: ([0-9.]+) us", text)
+    if mm:
+        out["fwd"] = float(mm.group(1))
+    mm = re.search(r"Backward \(sum of the averages of its \d+ kernels per call\): ([0-9.]+) us", text)
+    if mm:
+        out["bwd"] = float(mm.group(1))
     return out or None
 
 
@@ -557,7 +578,12 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": None if traffic is None or dom_name not in traffic else traffic[dom_name],
                 "kernel": "msda_backward (all its kernels)" if dom_name == "bwd" else "fwd_kernel",
-                "alg_bytes_per_launch": dom_b, "alg_bytes_per_point": dom_b / pts}
+                "alg_bytes_per_launch": dom_b, "alg_bytes_per_point": dom_b / pts,
+                "event_us_mean": dom["us_mean"]}
+    traced = traced_durations()
+    # the same pass in the committed kernel-trace summary (None if that was
+    # taken on another kernel source)
+    roofline["trace_us_mean"] = None if traced is None else traced.get(dom_name)
 
     result = {
         "metric": "sampled points/sec (N*Lq*M*L*K), forward + backward",
