@@ -113,9 +113,11 @@ def _dims(value, loc, attn, grouped=False):
     return (N, S, M, D, L, Lq, K, M2) if grouped else (N, S, M, D, L, Lq, K)
 
 
-def _device_tensor(t, what, dtype=None):
+def _device_tensor(t, what, dtype=None, device=None):
     if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
         raise ValueError(f"{what} must be a device tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{what} is on {t.device}, value on {device}: all tensors of a call share one GPU")
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{what} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
@@ -137,15 +139,15 @@ def msda_forward(value, spatial_shapes, level_start, loc, attn, out=None, stream
     lib = load_library()
     _device_tensor(value, "value")
     dt = _dtype_code(value.dtype)
-    _device_tensor(loc, "loc", torch.float32)
-    _device_tensor(attn, "attn", torch.float32)
+    _device_tensor(loc, "loc", torch.float32, device=value.device)
+    _device_tensor(attn, "attn", torch.float32, device=value.device)
     N, S, M, D, L, Lq, K = _dims(value, loc, attn)
     ss = _host_i64(spatial_shapes, (L, 2), "spatial_shapes")
     ls = _host_i64(level_start, (L,), "level_start")
     if out is None:
         out = torch.empty((N, Lq, M, D), dtype=value.dtype, device=value.device)
     else:
-        _device_tensor(out, "out", value.dtype)
+        _device_tensor(out, "out", value.dtype, device=value.device)
         if tuple(out.shape) != (N, Lq, M, D):
             raise ValueError(f"out must be {(N, Lq, M, D)}")
     with torch.cuda.device(value.device):
@@ -185,9 +187,9 @@ def msda_backward(value, spatial_shapes, level_start, loc, attn, grad_out, grad_
     lib = load_library()
     _device_tensor(value, "value")
     dt = _dtype_code(value.dtype)
-    _device_tensor(loc, "loc", torch.float32)
-    _device_tensor(attn, "attn", torch.float32)
-    _device_tensor(grad_out, "grad_out", value.dtype)
+    _device_tensor(loc, "loc", torch.float32, device=value.device)
+    _device_tensor(attn, "attn", torch.float32, device=value.device)
+    _device_tensor(grad_out, "grad_out", value.dtype, device=value.device)
     N, S, M, D, L, Lq, K = _dims(value, loc, attn)
     if tuple(grad_out.shape) != (N, Lq, M, D):
         raise ValueError(f"grad_out must be {(N, Lq, M, D)}")
@@ -203,14 +205,14 @@ def msda_backward(value, spatial_shapes, level_start, loc, attn, grad_out, grad_
     for t, name, shape in ((grad_value, "grad_value", (N, S, M, D)),
                            (grad_loc, "grad_loc", (N, Lq, M, L, K, 2)),
                            (grad_attn, "grad_attn", (N, Lq, M, L, K))):
-        _device_tensor(t, name, torch.float32)
+        _device_tensor(t, name, torch.float32, device=value.device)
         if tuple(t.shape) != shape:
             raise ValueError(f"{name} must be {shape}")
     need = msda_backward_workspace_size(ss, ls, N, S, M, D, L, Lq, K, dt)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     else:
-        _device_tensor(workspace, "workspace", torch.uint8)
+        _device_tensor(workspace, "workspace", torch.uint8, device=value.device)
     with torch.cuda.device(dev):
         s = torch.cuda.current_stream().cuda_stream if stream is None else int(stream)
         _raise(lib.msda_backward(value.data_ptr(), ss.ctypes.data, ls.ctypes.data, loc.data_ptr(),
@@ -244,14 +246,14 @@ def msda_fused_forward(value, spatial_shapes, level_start, ref, offsets, logits,
     _device_tensor(value, "value")
     dt = _dtype_code(value.dtype)
     for t, name in ((ref, "ref"), (offsets, "offsets"), (logits, "logits")):
-        _device_tensor(t, name, torch.float32)
+        _device_tensor(t, name, torch.float32, device=value.device)
     N, S, M, D, L, Lq, K, rd, G = _fused_dims(value, ref, offsets, logits)
     ss = _host_i64(spatial_shapes, (L, 2), "spatial_shapes")
     ls = _host_i64(level_start, (L,), "level_start")
     if out is None:
         out = torch.empty((N, Lq, M, D), dtype=value.dtype, device=value.device)
     else:
-        _device_tensor(out, "out", value.dtype)
+        _device_tensor(out, "out", value.dtype, device=value.device)
         if tuple(out.shape) != (N, Lq, M, D):
             raise ValueError(f"out must be {(N, Lq, M, D)}")
     with torch.cuda.device(value.device):
@@ -271,8 +273,8 @@ def msda_fused_backward(value, spatial_shapes, level_start, ref, offsets, logits
     _device_tensor(value, "value")
     dt = _dtype_code(value.dtype)
     for t, name in ((ref, "ref"), (offsets, "offsets"), (logits, "logits")):
-        _device_tensor(t, name, torch.float32)
-    _device_tensor(grad_out, "grad_out", value.dtype)
+        _device_tensor(t, name, torch.float32, device=value.device)
+    _device_tensor(grad_out, "grad_out", value.dtype, device=value.device)
     N, S, M, D, L, Lq, K, rd, G = _fused_dims(value, ref, offsets, logits)
     if tuple(grad_out.shape) != (N, Lq, M, D):
         raise ValueError(f"grad_out must be {(N, Lq, M, D)}")
@@ -292,14 +294,14 @@ def msda_fused_backward(value, spatial_shapes, level_start, ref, offsets, logits
     if grad_ref is not None:
         outs.append((grad_ref, "grad_ref", (N, Lq, rd)))
     for t, name, shape in outs:
-        _device_tensor(t, name, torch.float32)
+        _device_tensor(t, name, torch.float32, device=value.device)
         if tuple(t.shape) != shape:
             raise ValueError(f"{name} must be {shape}")
     need = msda_fused_backward_workspace_size(ss, ls, N, S, G, M // G * D, L, Lq, K, dt)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     else:
-        _device_tensor(workspace, "workspace", torch.uint8)
+        _device_tensor(workspace, "workspace", torch.uint8, device=value.device)
     with torch.cuda.device(dev):
         s = torch.cuda.current_stream().cuda_stream if stream is None else int(stream)
         _raise(lib.msda_fused_backward(value.data_ptr(), ss.ctypes.data, ls.ctypes.data, ref.data_ptr(), rd,
@@ -317,15 +319,15 @@ def msda_grouped_forward(value, spatial_shapes, level_start, loc, attn, out=None
     lib = load_library()
     _device_tensor(value, "value")
     dt = _dtype_code(value.dtype)
-    _device_tensor(loc, "loc", torch.float32)
-    _device_tensor(attn, "attn", torch.float32)
+    _device_tensor(loc, "loc", torch.float32, device=value.device)
+    _device_tensor(attn, "attn", torch.float32, device=value.device)
     N, S, M, D, L, Lq, K, G = _dims(value, loc, attn, grouped=True)
     ss = _host_i64(spatial_shapes, (L, 2), "spatial_shapes")
     ls = _host_i64(level_start, (L,), "level_start")
     if out is None:
         out = torch.empty((N, Lq, M, D), dtype=value.dtype, device=value.device)
     else:
-        _device_tensor(out, "out", value.dtype)
+        _device_tensor(out, "out", value.dtype, device=value.device)
         if tuple(out.shape) != (N, Lq, M, D):
             raise ValueError(f"out must be {(N, Lq, M, D)}")
     with torch.cuda.device(value.device):
@@ -342,9 +344,9 @@ def msda_grouped_backward(value, spatial_shapes, level_start, loc, attn, grad_ou
     lib = load_library()
     _device_tensor(value, "value")
     dt = _dtype_code(value.dtype)
-    _device_tensor(loc, "loc", torch.float32)
-    _device_tensor(attn, "attn", torch.float32)
-    _device_tensor(grad_out, "grad_out", value.dtype)
+    _device_tensor(loc, "loc", torch.float32, device=value.device)
+    _device_tensor(attn, "attn", torch.float32, device=value.device)
+    _device_tensor(grad_out, "grad_out", value.dtype, device=value.device)
     N, S, M, D, L, Lq, K, G = _dims(value, loc, attn, grouped=True)
     if tuple(grad_out.shape) != (N, Lq, M, D):
         raise ValueError(f"grad_out must be {(N, Lq, M, D)}")
@@ -360,7 +362,7 @@ def msda_grouped_backward(value, spatial_shapes, level_start, loc, attn, grad_ou
     for t, name, shape in ((grad_value, "grad_value", (N, S, M, D)),
                            (grad_loc, "grad_loc", (N, Lq, G, L, K, 2)),
                            (grad_attn, "grad_attn", (N, Lq, G, L, K))):
-        _device_tensor(t, name, torch.float32)
+        _device_tensor(t, name, torch.float32, device=value.device)
         if tuple(t.shape) != shape:
             raise ValueError(f"{name} must be {shape}")
     need = ctypes.c_size_t(0)
@@ -369,7 +371,7 @@ def msda_grouped_backward(value, spatial_shapes, level_start, loc, attn, grad_ou
     if workspace is None:
         workspace = torch.empty(max(need.value, 1), dtype=torch.uint8, device=dev)
     else:
-        _device_tensor(workspace, "workspace", torch.uint8)
+        _device_tensor(workspace, "workspace", torch.uint8, device=value.device)
     with torch.cuda.device(dev):
         s = torch.cuda.current_stream().cuda_stream if stream is None else int(stream)
         _raise(lib.msda_grouped_backward(value.data_ptr(), ss.ctypes.data, ls.ctypes.data, loc.data_ptr(),
