@@ -370,7 +370,10 @@ def grouped_passes(msda, torch, dev, steps, rotate, groups=(1, 2, 4)):
     return res
 
 
-def config_passes(msda, torch, dev, steps):
+CONFIG_PASSES = (("batched_encoder_fwd_bf16", False, 2), ("encoder_bwd", True, 3), ("encoder_bwd_k8", True, 2))
+
+
+def config_passes(msda, torch, dev, steps, only=None):
     """The other configurations of the workload table, timed the same way
     (HIP events around each call, buffer sets cycled so inputs come from HBM):
     batched encoder forward in bf16 (N=8) and the encoder backward at N=2 with
@@ -388,8 +391,9 @@ def config_passes(msda, torch, dev, steps):
 
     stream = torch.cuda.current_stream()
     res = {}
-    for name, backward, rotate in (("batched_encoder_fwd_bf16", False, 2), ("encoder_bwd", True, 3),
-                                   ("encoder_bwd_k8", True, 2)):
+    for name, backward, rotate in CONFIG_PASSES:
+        if only is not None and name != only:
+            continue
         w = config_workload(name)
         d = w.dims
         ss, ls = w.spatial_shapes, w.level_start
@@ -457,6 +461,11 @@ def main():
                          "e.g. under a profiler")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 256 MiB device copy (HBM counter calibration)")
+    ap.add_argument("--only", default=None,
+                    choices=["decoder_latency", "fused_inputs", "deformable_groups"] +
+                    [c[0] for c in CONFIG_PASSES],
+                    help="run only this secondary section or configuration and print its result "
+                         "(e.g. under a profiler); no main step")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -472,6 +481,21 @@ def main():
 
     import scale_deformable_attention_msda_amd as msda
     from workloads import config_workload
+
+    if args.only is not None:
+        dev = torch.device("cuda:0")
+        torch.cuda.set_device(dev)
+        steps = min(args.steps, 20)
+        if args.only == "decoder_latency":
+            res = decoder_latency(msda, torch, dev)
+        elif args.only == "fused_inputs":
+            res = fused_passes(msda, torch, dev, min(args.steps, 30), args.rotate)
+        elif args.only == "deformable_groups":
+            res = grouped_passes(msda, torch, dev, steps, args.rotate)
+        else:
+            res = config_passes(msda, torch, dev, steps, only=args.only)[args.only]
+        print(json.dumps({"section": args.only, "result": res}))
+        return
 
     w = config_workload("encoder_fwd", with_grad=True)
     d = w.dims

@@ -925,8 +925,13 @@ __global__ __launch_bounds__(kBlock) void bin_kernel(const Params p) {
 // a tile gives ceil(count / kPartEntries) items, at least one (an empty tile's
 // item writes its zeros). Tiles with several items are listed, in tile order
 // (a third prefix sum gives each its slot), so that they can be zeroed first.
+constexpr int kScanSplitCap = 2048;  // split tiles whose items the whole scan workgroup writes
+
 __global__ __launch_bounds__(1024) void scan_kernel(const Params p) {
   __shared__ uint32_t wsum_c[16], wsum_q[16], wsum_s[16], wsum_u[16];
+  // split tile i: tile, first entry, entry count, first item (before the
+  // list's reversal); filled by the tiles' owners, read by every thread
+  __shared__ uint4 ssplit[kScanSplitCap];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int per = (p.T + 1023) / 1024;
   const int t0 = tid * per, t1 = min(p.T, t0 + per);
@@ -983,24 +988,46 @@ __global__ __launch_bounds__(1024) void scan_kernel(const Params p) {
   uint4 *items = reinterpret_cast<uint4 *>(p.ws.work_item);
   // Work items: every split tile's items first (the longest work starts
   // first), coarse levels first (tiles in reverse order), then one item per
-  // remaining tile, also in reverse tile order.
+  // remaining tile, also in reverse tile order. With at most kScanSplitCap
+  // split tiles their items are written by the whole workgroup (a crowded
+  // tile has tens of items, all of one thread's run otherwise).
+  const bool shared_split = ts <= (uint32_t)kScanSplitCap;
   for (int t = t0; t < t1; ++t) {
     const uint32_t c = p.ws.tile_count[t];
     const uint32_t parts = parts_of(c);
     p.ws.tile_start[t] = start;
     p.ws.tile_cursor[t] = start;
     if (parts > 1) {
-      p.ws.split_list[sb++] = (uint32_t)t;
-      for (uint32_t k = 0; k < parts; ++k) {
-        const uint32_t e0 = start + k * kPartEntries;
-        items[tq - 1 - (qb + k)] = make_uint4((uint32_t)t, e0, min(e0 + (uint32_t)kPartEntries, start + c), 1u);
+      if (shared_split) {
+        ssplit[sb] = make_uint4((uint32_t)t, start, c, qb);
+      } else {
+        for (uint32_t k = 0; k < parts; ++k) {
+          const uint32_t e0 = start + k * kPartEntries;
+          items[tq - 1 - (qb + k)] = make_uint4((uint32_t)t, e0, min(e0 + (uint32_t)kPartEntries, start + c), 1u);
+        }
       }
+      p.ws.split_list[sb++] = (uint32_t)t;
       qb += parts;
     } else {
       items[tq + tu - 1 - ub] = make_uint4((uint32_t)t, start, start + c, 0u);
       ++ub;
     }
     start += c;
+  }
+  if (shared_split) {
+    __syncthreads();
+    // item j of the split group belongs to the last split tile whose first
+    // item is <= j (first items ascend with the split index)
+    for (uint32_t j = (uint32_t)tid; j < tq; j += 1024u) {
+      uint32_t lo = 0, hi = ts - 1;
+      while (lo < hi) {
+        const uint32_t mid = (lo + hi + 1) >> 1;
+        if (ssplit[mid].w <= j) lo = mid; else hi = mid - 1;
+      }
+      const uint4 sp = ssplit[lo];
+      const uint32_t e0 = sp.y + (j - sp.w) * kPartEntries;
+      items[tq - 1 - j] = make_uint4(sp.x, e0, min(e0 + (uint32_t)kPartEntries, sp.y + sp.z), 1u);
+    }
   }
   if (tid == 0) {
     p.ws.tile_start[p.T] = tc;
