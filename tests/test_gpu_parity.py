@@ -214,6 +214,21 @@ def test_hot_shapes_with_odd_point_counts(dtype):
     assert_grad_loc(gl, rgl, w.spatial_shapes)
 
 
+def test_large_map_counts_tiles_in_global_memory():
+    """A 400x400 level has 2500 8x8 tiles per (image, head), more than the
+    binning passes count in LDS, so they count and place entries with one
+    global atomic each; 24000 queries of 4 points keep the launch on the
+    sorted (dense) grad_value path."""
+    w = uniform_workload(N=1, shapes=((400, 400),), Lq=24000, M=2, D=8, K=4, seed=310, with_grad=True)
+    note("one 400x400 level: 2500 tiles per (image, head), dense backward")
+    assert_f32("out", to_f64(gpu_forward(w)), msda_forward(*_oracle_args(w)))
+    gv, gl, ga = (to_f64(t) for t in gpu_backward(w))
+    rgv, rgl, rga = msda_backward(*_oracle_args(w), w.grad_out)
+    assert_f32("grad_value", gv, rgv)
+    assert_f32("grad_attn", ga, rga)
+    assert_grad_loc(gl, rgl, w.spatial_shapes)
+
+
 def test_empty_problems():
     w = uniform_workload(N=1, shapes=((4, 4),), Lq=3, M=2, D=4, K=2, seed=300, with_grad=True)
     note("empty problems: Lq = 0 and N = 0")
