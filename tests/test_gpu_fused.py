@@ -142,15 +142,15 @@ def test_fused_backward_decoder_full_config(ref_dim, dtype):
     _check_grads(w, got, ref, w.ref, w.offsets)
 
 
-@pytest.mark.parametrize("ref_dim", [2, 4])
-def test_fused_hot_shapes_with_odd_point_counts(ref_dim):
-    """40000 pairs of D=32 fp32 heads select the launch shapes whose sample
+@pytest.mark.parametrize("ref_dim,dtype", [(2, "f32"), (4, "f32"), (2, "bf16")])
+def test_fused_hot_shapes_with_odd_point_counts(ref_dim, dtype):
+    """40000 pairs of D=32 heads select the launch shapes whose sample
     pass batches two samples' corner loads per lane; L*K = 9 leaves the last
     batch of each chunk half empty and takes the softmax from per-pair
     statistics (L*K not a power of two)."""
     w = fused_workload("decoder", N=1, shapes=((24, 40), (12, 20), (6, 10)), Lq=5000, M=8, D=32, K=3,
-                       ref_dim=ref_dim, dtype="f32", seed=110 + ref_dim, with_grad=True)
-    note(f"fused hot launch shapes with L*K=9, ref_dim={ref_dim}, 40000 pairs")
+                       ref_dim=ref_dim, dtype=dtype, seed=110 + ref_dim, with_grad=True)
+    note(f"fused hot launch shapes with L*K=9, ref_dim={ref_dim}, {dtype}, 40000 pairs")
     value, ref_t, off, logits, _ = _dev(w)
     out = to_f64(msda.msda_fused_forward(value, w.spatial_shapes, w.level_start, ref_t, off, logits))
     _check_out(w, out, msda_fused_forward(*_oracle_args(w)))
