@@ -1,5 +1,6 @@
 """Helpers of the GPU parity tests: move workloads to the device, run the HIP
 path through the binding, and compare with the fp64 oracle."""
+import os
 import sys
 
 import numpy as np
@@ -48,12 +49,26 @@ def gpu_backward(w, device="cuda:0"):
     return gv, gl, ga
 
 
+# every parity comparison of the session: (test, quantity, error, raw or None,
+# max |g - r| / max(1, |r|)); summarised at the end of the run (conftest.py)
+ERRORS = []
+
+
+def _record(name, err, raw, got, ref):
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rel = float(np.max(np.abs(got - ref) / np.maximum(1.0, np.abs(ref)))) if ref.size else 0.0
+    test = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
+    ERRORS.append((test, name, err, raw, rel))
+
+
 def max_abs(got, ref):
     return float(np.max(np.abs(np.asarray(got, np.float64) - np.asarray(ref, np.float64)))) if np.size(ref) else 0.0
 
 
 def assert_f32(name, got, ref, atol=1e-5):
     err = max_abs(got, ref)
+    _record(name, err, None, got, ref)
     assert np.all(np.isfinite(got)), f"{name}: non-finite values"
     assert err <= atol, f"{name}: max-abs error {err:.3e} > {atol:.1e}"
     return err
@@ -73,6 +88,7 @@ def assert_grad_loc(got, ref, spatial_shapes, atol=1e-5):
     """max-abs in pixel units; the raw error is reported alongside."""
     e_px = max_abs(grad_loc_pixels(got, spatial_shapes), grad_loc_pixels(ref, spatial_shapes))
     e_raw = max_abs(got, ref)
+    _record("grad_loc (pixel units)", e_px, e_raw, got, ref)
     assert np.all(np.isfinite(got)), "grad_loc: non-finite values"
     assert e_px <= atol, f"grad_loc: max-abs (pixel units) {e_px:.3e} > {atol:.1e}; raw {e_raw:.3e}"
     return e_px, e_raw
@@ -81,6 +97,7 @@ def assert_grad_loc(got, ref, spatial_shapes, atol=1e-5):
 def assert_normwise(name, got, ref, rtol=2e-2):
     ref = np.asarray(ref, np.float64)
     err = max_abs(got, ref) / max(float(np.max(np.abs(ref))), 1e-30)
+    _record(name + " (normwise)", err, max_abs(got, ref), got, ref)
     assert err <= rtol, f"{name}: normwise error {err:.3e} > {rtol:.1e}"
     return err
 
