@@ -370,15 +370,17 @@ def grouped_passes(msda, torch, dev, steps, rotate, groups=(1, 2, 4)):
     return res
 
 
-CONFIG_PASSES = (("batched_encoder_fwd_bf16", False, 2), ("encoder_bwd", True, 3), ("encoder_bwd_k8", True, 2))
+CONFIG_PASSES = (("batched_encoder_fwd_bf16", False, 2), ("encoder_bwd", True, 3), ("encoder_bwd_k8", True, 2),
+                 ("encoder_bwd_bf16", True, 3))
 
 
 def config_passes(msda, torch, dev, steps, only=None):
     """The other configurations of the workload table, timed the same way
     (HIP events around each call, buffer sets cycled so inputs come from HBM):
-    batched encoder forward in bf16 (N=8) and the encoder backward at N=2 with
-    K=4 and K=8. Algorithmic bytes: every input read once, every output
-    written once, value counted in full (every row is sampled)."""
+    batched encoder forward in bf16 (N=8), the encoder backward at N=2 with
+    K=4 and K=8, and the same K=4 backward with bf16 value and grad_out.
+    Algorithmic bytes: every input read once, every output written once,
+    value counted in full (every row is sampled)."""
     import numpy as np
 
     from workloads import config_workload
@@ -394,7 +396,12 @@ def config_passes(msda, torch, dev, steps, only=None):
     for name, backward, rotate in CONFIG_PASSES:
         if only is not None and name != only:
             continue
-        w = config_workload(name)
+        if name == "encoder_bwd_bf16":
+            from workloads import encoder_workload
+            w = encoder_workload(N=2, M=8, D=32, K=4, dtype="bf16", seed=5, with_grad=True,
+                                 name="encoder_bwd_bf16")
+        else:
+            w = config_workload(name)
         d = w.dims
         ss, ls = w.spatial_shapes, w.level_start
         elem = 2 if w.dtype == "bf16" else 4
