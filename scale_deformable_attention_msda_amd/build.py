@@ -35,5 +35,18 @@ def build(verbose=False, extra_flags=()):
     return LIB
 
 
+def build_c_abi_check(source, exe):
+    """Compile a host program that calls the library through include/msda.h
+    (HIP runtime, no torch) and links libmsda.so next to it by rpath."""
+    rpath = os.path.relpath(HERE, os.path.dirname(os.path.abspath(exe)))
+    cmd = [hipcc(), "-O2", "-std=c++17", "-I", INCLUDE, source, "-o", exe + ".tmp",
+           "-L", HERE, "-lmsda", "-Wl,-rpath,$ORIGIN/" + rpath]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("C-ABI check program build failed:\n" + " ".join(cmd) + "\n" + res.stderr)
+    os.replace(exe + ".tmp", exe)
+    return exe
+
+
 if __name__ == "__main__":
     print(build(verbose=True))

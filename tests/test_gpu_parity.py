@@ -7,6 +7,9 @@ raw gradient is already above 1e-5. bfloat16 outputs: normwise
 max|gpu - oracle| / max|oracle| <= 2e-2, and additionally within one bf16 ulp
 (+1e-5) elementwise, since the fp32 sum is rounded once to bf16.
 """
+import os
+import subprocess
+
 import numpy as np
 import pytest
 
@@ -227,6 +230,17 @@ def test_large_map_counts_tiles_in_global_memory():
     assert_f32("grad_value", gv, rgv)
     assert_f32("grad_attn", ga, rga)
     assert_grad_loc(gl, rgl, w.spatial_shapes)
+
+
+def test_native_program_through_the_c_abi():
+    """tests/c/abi_device.cpp (built with the library): plain HIP buffers and
+    a stream of its own, no torch, forward and backward through the C ABI,
+    checked against closed forms (constant map, adjoint identity)."""
+    exe = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c", "abi_device")
+    assert os.path.exists(exe), f"{exe} is missing: __graft_entry__.build() compiles it"
+    note("native C++ program through the C ABI (hipMalloc buffers, own stream)")
+    res = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    assert res.returncode == 0 and res.stdout.strip().endswith("OK"), res.stdout + res.stderr
 
 
 def test_empty_problems():
