@@ -8,6 +8,7 @@ anything elsewhere.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 
 import numpy as np
@@ -79,13 +80,44 @@ def _raise(status):
         raise MSDAError(status, msda_status_string(status))
 
 
+_current_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _call(device, stream, fn, *args, writes=()):
+    """Calls entry point ``fn`` with ``args`` followed by a stream handle: ``stream``
+    when given, else torch's current stream on ``device``. ``device`` is made
+    current for the call (the common case, already current, costs one query).
+
+    With an explicit ``stream`` the tensors in ``writes`` (outputs and workspace,
+    which torch allocated on its current stream) are recorded as used on that
+    stream, so that the caching allocator does not hand their memory out again
+    before the work queued there has finished."""
+    idx = device.index
+    if torch.cuda.current_device() != idx:
+        with torch.cuda.device(idx):
+            return _call(device, stream, fn, *args, writes=writes)
+    if stream is None:
+        if _current_raw_stream is not None:
+            return fn(*args, _current_raw_stream(idx))
+        return fn(*args, torch.cuda.current_stream(idx).cuda_stream)
+    s = int(stream)
+    status = fn(*args, s)
+    ext = torch.cuda.ExternalStream(s, device=device)
+    for t in writes:
+        if t is not None:
+            t.record_stream(ext)
+    return status
+
+
 def _host_i64(a, shape, what):
+    if type(a) is np.ndarray and a.dtype == np.int64 and a.shape == shape and a.flags.c_contiguous:
+        return a
     if isinstance(a, torch.Tensor):
         if a.device.type != "cpu":
             raise ValueError(f"{what} must be a host array: the library reads it during the call")
         a = a.numpy()
     arr = np.ascontiguousarray(np.asarray(a, dtype=np.int64))
-    if arr.size != int(np.prod(shape)):
+    if arr.size != math.prod(shape):
         raise ValueError(f"{what} has {arr.size} entries, expected shape {shape}")
     return arr.reshape(shape)
 
@@ -150,10 +182,9 @@ def msda_forward(value, spatial_shapes, level_start, loc, attn, out=None, stream
         _device_tensor(out, "out", value.dtype, device=value.device)
         if tuple(out.shape) != (N, Lq, M, D):
             raise ValueError(f"out must be {(N, Lq, M, D)}")
-    with torch.cuda.device(value.device):
-        s = torch.cuda.current_stream().cuda_stream if stream is None else int(stream)
-        _raise(lib.msda_forward(value.data_ptr(), ss.ctypes.data, ls.ctypes.data, loc.data_ptr(),
-                                attn.data_ptr(), out.data_ptr(), N, S, M, D, L, Lq, K, dt, s))
+    _raise(_call(value.device, stream, lib.msda_forward,
+            value.data_ptr(), ss.ctypes.data, ls.ctypes.data, loc.data_ptr(), attn.data_ptr(),
+            out.data_ptr(), N, S, M, D, L, Lq, K, dt, writes=(out,)))
     return out
 
 
@@ -213,12 +244,11 @@ def msda_backward(value, spatial_shapes, level_start, loc, attn, grad_out, grad_
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     else:
         _device_tensor(workspace, "workspace", torch.uint8, device=value.device)
-    with torch.cuda.device(dev):
-        s = torch.cuda.current_stream().cuda_stream if stream is None else int(stream)
-        _raise(lib.msda_backward(value.data_ptr(), ss.ctypes.data, ls.ctypes.data, loc.data_ptr(),
-                                 attn.data_ptr(), grad_out.data_ptr(), grad_value.data_ptr(),
-                                 grad_loc.data_ptr(), grad_attn.data_ptr(), N, S, M, D, L, Lq, K,
-                                 dt, workspace.data_ptr(), workspace.numel(), s))
+    _raise(_call(dev, stream, lib.msda_backward,
+            value.data_ptr(), ss.ctypes.data, ls.ctypes.data, loc.data_ptr(), attn.data_ptr(),
+            grad_out.data_ptr(), grad_value.data_ptr(), grad_loc.data_ptr(), grad_attn.data_ptr(), N, S, M,
+            D, L, Lq, K, dt, workspace.data_ptr(), workspace.numel(),
+            writes=(grad_value, grad_loc, grad_attn, workspace)))
     return grad_value, grad_loc, grad_attn
 
 
@@ -256,11 +286,9 @@ def msda_fused_forward(value, spatial_shapes, level_start, ref, offsets, logits,
         _device_tensor(out, "out", value.dtype, device=value.device)
         if tuple(out.shape) != (N, Lq, M, D):
             raise ValueError(f"out must be {(N, Lq, M, D)}")
-    with torch.cuda.device(value.device):
-        s = torch.cuda.current_stream().cuda_stream if stream is None else int(stream)
-        _raise(lib.msda_fused_forward(value.data_ptr(), ss.ctypes.data, ls.ctypes.data, ref.data_ptr(), rd,
-                                      offsets.data_ptr(), logits.data_ptr(), out.data_ptr(), N, S, G,
-                                      M // G * D, L, Lq, K, dt, s))
+    _raise(_call(value.device, stream, lib.msda_fused_forward,
+            value.data_ptr(), ss.ctypes.data, ls.ctypes.data, ref.data_ptr(), rd, offsets.data_ptr(),
+            logits.data_ptr(), out.data_ptr(), N, S, G, M // G * D, L, Lq, K, dt, writes=(out,)))
     return out
 
 
@@ -302,14 +330,12 @@ def msda_fused_backward(value, spatial_shapes, level_start, ref, offsets, logits
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     else:
         _device_tensor(workspace, "workspace", torch.uint8, device=value.device)
-    with torch.cuda.device(dev):
-        s = torch.cuda.current_stream().cuda_stream if stream is None else int(stream)
-        _raise(lib.msda_fused_backward(value.data_ptr(), ss.ctypes.data, ls.ctypes.data, ref.data_ptr(), rd,
-                                       offsets.data_ptr(), logits.data_ptr(), grad_out.data_ptr(),
-                                       grad_value.data_ptr(), grad_offsets.data_ptr(), grad_logits.data_ptr(),
-                                       grad_ref.data_ptr() if grad_ref is not None else None,
-                                       N, S, G, M // G * D, L, Lq, K, dt, workspace.data_ptr(), workspace.numel(),
-                                       s))
+    _raise(_call(dev, stream, lib.msda_fused_backward,
+            value.data_ptr(), ss.ctypes.data, ls.ctypes.data, ref.data_ptr(), rd, offsets.data_ptr(),
+            logits.data_ptr(), grad_out.data_ptr(), grad_value.data_ptr(), grad_offsets.data_ptr(),
+            grad_logits.data_ptr(), grad_ref.data_ptr() if grad_ref is not None else None, N, S, G,
+            M // G * D, L, Lq, K, dt, workspace.data_ptr(), workspace.numel(),
+            writes=(grad_value, grad_offsets, grad_logits, grad_ref, workspace)))
     return grad_value, grad_offsets, grad_logits, grad_ref
 
 
@@ -330,10 +356,9 @@ def msda_grouped_forward(value, spatial_shapes, level_start, loc, attn, out=None
         _device_tensor(out, "out", value.dtype, device=value.device)
         if tuple(out.shape) != (N, Lq, M, D):
             raise ValueError(f"out must be {(N, Lq, M, D)}")
-    with torch.cuda.device(value.device):
-        s = torch.cuda.current_stream().cuda_stream if stream is None else int(stream)
-        _raise(lib.msda_grouped_forward(value.data_ptr(), ss.ctypes.data, ls.ctypes.data, loc.data_ptr(),
-                                        attn.data_ptr(), out.data_ptr(), N, S, M, D, L, Lq, K, G, dt, s))
+    _raise(_call(value.device, stream, lib.msda_grouped_forward,
+            value.data_ptr(), ss.ctypes.data, ls.ctypes.data, loc.data_ptr(), attn.data_ptr(),
+            out.data_ptr(), N, S, M, D, L, Lq, K, G, dt, writes=(out,)))
     return out
 
 
@@ -372,12 +397,11 @@ def msda_grouped_backward(value, spatial_shapes, level_start, loc, attn, grad_ou
         workspace = torch.empty(max(need.value, 1), dtype=torch.uint8, device=dev)
     else:
         _device_tensor(workspace, "workspace", torch.uint8, device=value.device)
-    with torch.cuda.device(dev):
-        s = torch.cuda.current_stream().cuda_stream if stream is None else int(stream)
-        _raise(lib.msda_grouped_backward(value.data_ptr(), ss.ctypes.data, ls.ctypes.data, loc.data_ptr(),
-                                         attn.data_ptr(), grad_out.data_ptr(), grad_value.data_ptr(),
-                                         grad_loc.data_ptr(), grad_attn.data_ptr(), N, S, M, D, L, Lq, K, G,
-                                         dt, workspace.data_ptr(), workspace.numel(), s))
+    _raise(_call(dev, stream, lib.msda_grouped_backward,
+            value.data_ptr(), ss.ctypes.data, ls.ctypes.data, loc.data_ptr(), attn.data_ptr(),
+            grad_out.data_ptr(), grad_value.data_ptr(), grad_loc.data_ptr(), grad_attn.data_ptr(), N, S, M,
+            D, L, Lq, K, G, dt, workspace.data_ptr(), workspace.numel(),
+            writes=(grad_value, grad_loc, grad_attn, workspace)))
     return grad_value, grad_loc, grad_attn
 
 
