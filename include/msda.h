@@ -17,7 +17,8 @@
  *     coordinate is x = fmaf(loc_x, W_l, -0.5f), y = fmaf(loc_y, H_l, -0.5f),
  *     so pixel j's centre is at (j+0.5)/W_l.
  *   - zero padding: a corner outside the map reads 0; a sample contributes
- *     only if -1 <= x < W_l and -1 <= y < H_l (NaN never does).
+ *     only if -1 <= x < W_l and -1 <= y < H_l. A NaN or infinite coordinate
+ *     never does: that sample adds nothing and gets zero grad_loc and grad_attn.
  *   - at integer x or y the location gradient is the right-derivative
  *     (x0 = floor(x) everywhere).
  *   - pixel (i, j) of level l is row level_start[l] + i*W_l + j of value.

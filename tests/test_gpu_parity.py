@@ -7,6 +7,7 @@ raw gradient is already above 1e-5. bfloat16 outputs: normwise
 max|gpu - oracle| / max|oracle| <= 2e-2, and additionally within one bf16 ulp
 (+1e-5) elementwise, since the fp32 sum is rounded once to bf16.
 """
+import dataclasses
 import os
 import subprocess
 
@@ -230,6 +231,48 @@ def test_large_map_counts_tiles_in_global_memory():
     assert_f32("grad_value", gv, rgv)
     assert_f32("grad_attn", ga, rga)
     assert_grad_loc(gl, rgl, w.spatial_shapes)
+
+
+@pytest.mark.parametrize("kind,dtype", [("dense", "f32"), ("dense", "bf16"), ("sparse", "f32")])
+def test_non_finite_locations_contribute_nothing(kind, dtype):
+    """A location with a NaN, infinite or overflowing coordinate lies outside
+    every level: its sample adds nothing to out and gets zero grad_loc and
+    grad_attn, exactly as a location far outside the map (the oracle's input
+    here). Both grad_value routes: the sorted one (dense) and the atomic one."""
+    if kind == "dense":
+        w = encoder_workload(N=2, shapes=SMALL_LEVELS, M=8, D=32, K=4, dtype=dtype, seed=720,
+                             with_grad=True)
+    else:  # 40 queries x 16 samples stay below 32 samples per tile: per-sample atomics
+        w = decoder_workload(N=2, shapes=SMALL_LEVELS, Lq=40, dtype=dtype, seed=721, with_grad=True)
+    rng = np.random.default_rng(722)
+    flat = w.loc.reshape(-1, 2)
+    pick = rng.random(flat.shape[0]) < 0.1
+    bad = np.array([np.nan, np.inf, -np.inf, 3e38, -3e38], np.float32)
+    vals = bad[rng.integers(0, len(bad), size=(int(pick.sum()), 2))]
+    one = rng.random(len(vals)) < 0.5  # half keep one finite coordinate
+    axis = rng.integers(0, 2, size=len(vals))
+    vals[one, axis[one]] = flat[pick][one, axis[one]]
+    gpu_loc = flat.copy()
+    gpu_loc[pick] = vals
+    far = flat.copy()
+    far[pick] = -5.0
+    wg = dataclasses.replace(w, loc=gpu_loc.reshape(w.loc.shape))
+    wo = dataclasses.replace(w, loc=far.reshape(w.loc.shape))
+    note(f"non-finite locations ({int(pick.sum())} samples), {kind} backward, {dtype}")
+    out = gpu_forward(wg)
+    gv, gl, ga = gpu_backward(wg)
+    for t in (out, gv, gl, ga):
+        assert bool(torch.isfinite(t).all())
+    ref = msda_forward(*_oracle_args(wo))
+    if dtype == "f32":
+        assert_f32("out", to_f64(out), ref)
+    else:
+        _check_bf16_out(to_f64(out), ref)
+    rgv, rgl, rga = msda_backward(*_oracle_args(wo), wo.grad_out)
+    assert_f32("grad_value", to_f64(gv), rgv)
+    assert_f32("grad_attn", to_f64(ga), rga)
+    assert_grad_loc(to_f64(gl), rgl, w.spatial_shapes)
+    assert not to_f64(gl).reshape(-1, 2)[pick].any() and not to_f64(ga).reshape(-1)[pick].any()
 
 
 def test_native_program_through_the_c_abi():
