@@ -9,9 +9,11 @@ COCO feature maps). Inputs are resident in HBM before timing. Several buffer
 sets (inputs and outputs) are cycled so that no step finds its data in the
 256 MB Infinity Cache left behind by the previous one.
 
-Prints one JSON line: sampled points/s (N*Lq*M*L*K per step / step time),
-per-pass timings from HIP events on the launch stream, the HBM roofline of
-the dominant kernel and the fp64 CPU oracle's rate on a bounded sample.
+Prints one JSON line: sampled points/s (N*Lq*M*L*K per step / wall time of
+the timed steps, which carry no event markers), per-pass timings from HIP
+events on the launch stream (each pass launched back to back between two
+events), the HBM roofline of the dominant kernel and the fp64 CPU oracle's
+rate on a bounded sample.
 """
 import argparse
 import hashlib
@@ -222,6 +224,33 @@ def decoder_latency(msda, torch, dev, layers=6, reps=20):
     return res
 
 
+def time_launches(torch, fn, sets, steps):
+    """Per-launch times of fn over the buffer sets, cycled. The mean comes from
+    `steps` back-to-back launches with one event before the first and one after
+    the last, so no event marker sits between launches (a marker costs the GPU
+    ~4 us); the percentiles come from a second run with an event between
+    consecutive launches, so each of those includes one marker. Returns
+    (mean_ms, per_launch_ms array)."""
+    import numpy as np
+
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for i in range(steps):
+        fn(sets[i % len(sets)])
+    b.record(stream)
+    torch.cuda.synchronize()
+    mean_ms = a.elapsed_time(b) / steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        fn(sets[i % len(sets)])
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return mean_ms, np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+
+
 def copy_ceiling(torch, dev, reps=5):
     """Measured stream-copy ceiling: a 512 MiB device-to-device copy whose source
     and destination (1 GiB together) exceed the 256 MB Infinity Cache, timed with
@@ -301,22 +330,14 @@ def fused_passes(msda, torch, dev, steps, rotate):
         torch.div(gl, size[None, None, None, :, None, :], out=s["go"])
         torch.sum(gl, dim=(2, 3, 4), out=s["gr"])
 
-    stream = torch.cuda.current_stream()
     res = {"workload": "encoder shape as above from raw inputs: reference points at pixel centres, "
                        "N(0,2px) offsets, N(0,1) logits"}
     for name, fn in (("fwd", fwd), ("bwd", bwd), ("unfused_fwd", unfused_fwd), ("unfused_bwd", unfused_bwd)):
         for i in range(3):
             fn(sets[i % rotate])
-        torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-        for i in range(steps):
-            ev[i][0].record(stream)
-            fn(sets[i % rotate])
-            ev[i][1].record(stream)
-        torch.cuda.synchronize()
-        ms = np.array([a.elapsed_time(b) for a, b in ev])
-        res[name] = {"us_mean": round(float(ms.mean()) * 1e3, 2), "us_median": round(float(np.median(ms)) * 1e3, 2),
-                     "points_per_s": w.points / (float(ms.mean()) * 1e-3)}
+        mean_ms, ms = time_launches(torch, fn, sets[:rotate], steps)
+        res[name] = {"us_mean": round(mean_ms * 1e3, 2), "us_median_with_marker": round(float(np.median(ms)) * 1e3, 2),
+                     "points_per_s": w.points / (mean_ms * 1e-3)}
     return res
 
 
@@ -328,7 +349,6 @@ def grouped_passes(msda, torch, dev, steps, rotate, groups=(1, 2, 4)):
     from workloads import encoder_workload
 
     res = {"workload": "encoder shape as above, loc/attn per deformable group"}
-    stream = torch.cuda.current_stream()
     for G in groups:
         w = encoder_workload(N=1, M=8, D=32, K=4, seed=2, groups=G, with_grad=True)
         d = w.dims
@@ -354,16 +374,8 @@ def grouped_passes(msda, torch, dev, steps, rotate, groups=(1, 2, 4)):
         for name, fn in (("fwd", fwd), ("bwd", bwd)):
             for i in range(3):
                 fn(sets[i % rotate])
-            torch.cuda.synchronize()
-            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for _ in range(steps)]
-            for i in range(steps):
-                ev[i][0].record(stream)
-                fn(sets[i % rotate])
-                ev[i][1].record(stream)
-            torch.cuda.synchronize()
-            ms = np.array([a.elapsed_time(b) for a, b in ev])
-            entry[name + "_us_mean"] = round(float(ms.mean()) * 1e3, 2)
+            mean_ms, _ = time_launches(torch, fn, sets[:rotate], steps)
+            entry[name + "_us_mean"] = round(mean_ms * 1e3, 2)
         entry["points_per_s_fwd_bwd"] = w.points / ((entry["fwd_us_mean"] + entry["bwd_us_mean"]) * 1e-6)
         res[f"G={G}"] = entry
         del sets
@@ -391,7 +403,6 @@ def config_passes(msda, torch, dev, steps, only=None):
             return torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(dev)
         return torch.from_numpy(getattr(w, name)).to(dev)
 
-    stream = torch.cuda.current_stream()
     res = {}
     for name, backward, rotate in CONFIG_PASSES:
         if only is not None and name != only:
@@ -437,18 +448,11 @@ def config_passes(msda, torch, dev, steps, only=None):
 
         for i in range(3):
             run(sets[i % rotate])
-        torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-        for i in range(steps):
-            ev[i][0].record(stream)
-            run(sets[i % rotate])
-            ev[i][1].record(stream)
-        torch.cuda.synchronize()
-        ms = np.array([a.elapsed_time(b) for a, b in ev])
-        t = float(ms.mean()) * 1e-3
+        mean_ms, ms = time_launches(torch, run, sets[:rotate], steps)
+        t = mean_ms * 1e-3
         res[name] = {"workload": f"N={d['N']}, Lq={d['Lq']}, M={d['M']}, D={d['D']}, K={d['K']}, {w.dtype}, "
                                  f"{'backward' if backward else 'forward'}",
-                     "us_mean": round(t * 1e6, 2), "us_median": round(float(np.median(ms)) * 1e3, 2),
+                     "us_mean": round(t * 1e6, 2), "us_median_with_marker": round(float(np.median(ms)) * 1e3, 2),
                      "points_per_s": pts / t, "alg_bytes": alg, "alg_GBps": round(alg / t / 1e9, 1),
                      "hbm_frac": round(alg / t / 1e9 / HBM_PEAK_GBPS, 4)}
         del sets
@@ -551,25 +555,34 @@ def main():
         step(sets[i % args.rotate])
     torch.cuda.synchronize()
 
-    stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # The timed region: exactly `steps` forward + backward steps, nothing else
+    # on the stream (no event markers between the passes).
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        s = sets[i % args.rotate]
-        ev[i][0].record(stream)
-        msda.msda_forward(s["value"], ss, ls, s["loc"], s["attn"], out=s["out"])
-        ev[i][1].record(stream)
-        msda.msda_backward(s["value"], ss, ls, s["loc"], s["attn"], s["grad_out"],
-                           grad_value=s["gv"], grad_loc=s["gl"], grad_attn=s["ga"], workspace=s["ws"])
-        ev[i][2].record(stream)
+        step(sets[i % args.rotate])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-
-    fwd_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
-    bwd_ms = np.array([e[1].elapsed_time(e[2]) for e in ev])
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     value = pts / (ms_per_step * 1e-3)
+
+    # Per-pass breakdown: the same `steps` steps again, with an event between
+    # the passes and between steps (2 per step, chained), so each pass is
+    # timed where it runs in the step; each interval includes one marker.
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        s = sets[i % args.rotate]
+        msda.msda_forward(s["value"], ss, ls, s["loc"], s["attn"], out=s["out"])
+        ev[2 * i + 1].record(stream)
+        msda.msda_backward(s["value"], ss, ls, s["loc"], s["attn"], s["grad_out"],
+                           grad_value=s["gv"], grad_loc=s["gl"], grad_attn=s["ga"], workspace=s["ws"])
+        ev[2 * i + 2].record(stream)
+    torch.cuda.synchronize()
+    fwd_ms = np.array([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(args.steps)])
+    bwd_ms = np.array([ev[2 * i + 1].elapsed_time(ev[2 * i + 2]) for i in range(args.steps)])
 
     def pass_stats(ms, b):
         t = float(ms.mean()) * 1e-3
@@ -581,24 +594,22 @@ def main():
 
     fwd = pass_stats(fwd_ms, b_fwd)
     bwd = pass_stats(bwd_ms, b_bwd)
+
+    def fwd_only(s):
+        msda.msda_forward(s["value"], ss, ls, s["loc"], s["attn"], out=s["out"])
+
+    def bwd_only(s):
+        msda.msda_backward(s["value"], ss, ls, s["loc"], s["attn"], s["grad_out"],
+                           grad_value=s["gv"], grad_loc=s["gl"], grad_attn=s["ga"], workspace=s["ws"])
     copy_gbps = None if args.main_only else copy_ceiling(torch, dev)
     warm = None
     if not args.main_only:
-        # secondary: back-to-back steps on one buffer set (inputs left in the caches)
-        s0 = sets[0]
+        # secondary: back-to-back launches on one buffer set (inputs left in the caches)
+        s0 = sets[:1]
         for _ in range(3):
-            step(s0)
-        wev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(20)]
-        for e3 in wev:
-            e3[0].record(stream)
-            msda.msda_forward(s0["value"], ss, ls, s0["loc"], s0["attn"], out=s0["out"])
-            e3[1].record(stream)
-            msda.msda_backward(s0["value"], ss, ls, s0["loc"], s0["attn"], s0["grad_out"], grad_value=s0["gv"],
-                               grad_loc=s0["gl"], grad_attn=s0["ga"], workspace=s0["ws"])
-            e3[2].record(stream)
-        torch.cuda.synchronize()
-        warm = {"fwd_us_median": round(float(np.median([e3[0].elapsed_time(e3[1]) for e3 in wev])) * 1e3, 2),
-                "bwd_us_median": round(float(np.median([e3[1].elapsed_time(e3[2]) for e3 in wev])) * 1e3, 2)}
+            step(s0[0])
+        warm = {"fwd_us_mean": round(time_launches(torch, fwd_only, s0, 20)[0] * 1e3, 2),
+                "bwd_us_mean": round(time_launches(torch, bwd_only, s0, 20)[0] * 1e3, 2)}
     if copy_gbps:
         for st in (fwd, bwd):
             st["frac_of_copy_ceiling"] = round(st["alg_GBps"] / copy_gbps, 4)
