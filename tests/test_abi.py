@@ -206,6 +206,22 @@ def test_binding_rejects_host_tensors():
         msda.msda_forward(x, [[2, 2]], [0], loc, attn)
 
 
+def test_binding_host_arrays():
+    """spatial_shapes / level_start: an int64 C-contiguous array of the right
+    shape is passed through as is; other integer arrays, lists and CPU tensors
+    are converted; a wrong entry count raises before any library call."""
+    torch = pytest.importorskip("torch")
+    ss = np.array([[100, 167], [50, 84]], dtype=np.int64)
+    assert binding._host_i64(ss, (2, 2), "spatial_shapes") is ss
+    for a in (ss.astype(np.int32), ss.tolist(), torch.from_numpy(ss.copy()), np.asfortranarray(ss)):
+        got = binding._host_i64(a, (2, 2), "spatial_shapes")
+        assert got.dtype == np.int64 and got.flags.c_contiguous and np.array_equal(got, ss)
+    flat = binding._host_i64(np.array([0, 16700]), (2,), "level_start")
+    assert flat.shape == (2,) and flat.dtype == np.int64
+    with pytest.raises(ValueError, match="3 entries"):
+        binding._host_i64([0, 1, 2], (2,), "level_start")
+
+
 def test_header_compiles_as_c_and_links(tmp_path):
     """A plain C11 program (tests/c/abi_host.c) includes the header, links the
     library and runs its host-side paths: validation, status strings,
