@@ -85,7 +85,8 @@ _current_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 def _call(device, stream, fn, *args, writes=()):
     """Calls entry point ``fn`` with ``args`` followed by a stream handle: ``stream``
-    when given, else torch's current stream on ``device``. ``device`` is made
+    when given (a torch.cuda.Stream or a raw HIP stream handle), else torch's
+    current stream on ``device``. ``device`` is made
     current for the call (the common case, already current, costs one query).
 
     With an explicit ``stream`` the tensors in ``writes`` (outputs and workspace,
@@ -100,12 +101,16 @@ def _call(device, stream, fn, *args, writes=()):
         if _current_raw_stream is not None:
             return fn(*args, _current_raw_stream(idx))
         return fn(*args, torch.cuda.current_stream(idx).cuda_stream)
-    s = int(stream)
+    if isinstance(stream, torch.cuda.Stream):
+        s, used = stream.cuda_stream, stream
+    else:
+        s, used = int(stream), None
     status = fn(*args, s)
-    ext = torch.cuda.ExternalStream(s, device=device)
+    if used is None:
+        used = torch.cuda.ExternalStream(s, device=device)
     for t in writes:
         if t is not None:
-            t.record_stream(ext)
+            t.record_stream(used)
     return status
 
 

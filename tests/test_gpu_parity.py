@@ -403,8 +403,9 @@ def test_unaligned_value_and_stream():
 
 
 def test_explicit_stream_handle():
-    """A raw stream handle passed as ``stream`` is used in place of torch's current
-    stream, for the forward and the backward (its workspace comes from torch)."""
+    """A raw stream handle (or a torch stream) passed as ``stream`` is used in
+    place of torch's current stream, for the forward and the backward (its
+    workspace comes from torch)."""
     w = uniform_workload(N=1, shapes=((9, 7), (4, 5)), Lq=33, M=2, D=8, K=3, seed=710,
                          with_grad=True)
     value, loc, attn, grad_out = device_inputs(w)
@@ -421,12 +422,14 @@ def test_explicit_stream_handle():
     out = msda.msda_forward(value, w.spatial_shapes, w.level_start, loc, attn, stream=s.cuda_stream)
     gv, gl, ga = msda.msda_backward(value, w.spatial_shapes, w.level_start, loc, attn, grad_out,
                                     stream=s.cuda_stream)
+    out_s = msda.msda_forward(value, w.spatial_shapes, w.level_start, loc, attn, stream=s)  # a torch stream
     # Memory the backward's workspace came from must not be handed out again while the
     # side stream has not reached it: fill same-sized blocks on the current stream.
     junk = [torch.full((max(need, 1),), 255, dtype=torch.uint8, device="cuda") for _ in range(4)]
     s.synchronize()
     del junk
     assert_f32("out", to_f64(out), msda_forward(*_oracle_args(w)))
+    assert torch.equal(out, out_s)
     rv, rl, ra = msda_backward(*_oracle_args(w), w.grad_out)
     assert_f32("grad_value", to_f64(gv), rv)
     assert_grad_loc(to_f64(gl), rl, w.spatial_shapes)
