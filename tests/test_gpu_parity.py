@@ -546,6 +546,53 @@ def test_graph_capture_of_decoder_layers():
                 assert torch.allclose(a, b, rtol=0, atol=1e-5), (rep, k)
 
 
+def test_graph_capture_of_the_dense_backward():
+    """The tile-sorted backward (counters cleared by a fill kernel, count, scan,
+    scatter, grad_value items with split-tile atomics) captured in a HIP graph:
+    each replay, with new inputs copied into the captured buffers, eager work
+    and synchronisation in between, matches the oracle for those inputs."""
+    wls = [encoder_workload(N=2, shapes=SMALL_LEVELS, M=8, D=32, K=4, seed=730 + i, with_grad=True)
+           for i in range(2)]
+    d = wls[0].dims
+    ss, ls = wls[0].spatial_shapes, wls[0].level_start
+    tiles = sum(((h + 7) // 8) * ((w_ + 7) // 8) for h, w_ in SMALL_LEVELS)
+    assert d["Lq"] * d["L"] * d["K"] >= 32 * tiles  # the dense route
+    refs = [msda_backward(*_oracle_args(w), w.grad_out) for w in wls]
+    value, loc, attn, grad_out = device_inputs(wls[0])
+    gv, gl, ga = torch.empty_like(value), torch.empty_like(loc), torch.empty_like(attn)
+    ws = torch.empty(msda.msda_backward_workspace_size(ss, ls, d["N"], d["S"], d["M"], d["D"], d["L"], d["Lq"],
+                                                       d["K"]), dtype=torch.uint8, device="cuda")
+
+    def run():
+        msda.msda_backward(value, ss, ls, loc, attn, grad_out, grad_value=gv, grad_loc=gl, grad_attn=ga,
+                           workspace=ws)
+
+    note("graph capture: dense encoder backward, small maps, f32")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        run()
+    for rep in range(4):
+        w = wls[rep % 2]
+        for dst, src in ((value, w.value), (loc, w.loc), (attn, w.attn), (grad_out, w.grad_out)):
+            dst.copy_(torch.from_numpy(src))
+        for t in (gv, gl, ga):
+            t.fill_(float("nan"))
+        _ = (torch.randn(1024, 1024, device="cuda") @ torch.randn(1024, 1024, device="cuda")).sum()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        rgv, rgl, rga = refs[rep % 2]
+        assert_f32("grad_value", to_f64(gv), rgv)
+        assert_f32("grad_attn", to_f64(ga), rga)
+        assert_grad_loc(to_f64(gl), rgl, w.spatial_shapes)
+
+
 def test_batch_split_across_launches():
     """Images whose value slice exceeds 2^27 elements run one launch per image;
     every pointer (value, loc, attn, ref, outputs and gradients) is offset per
