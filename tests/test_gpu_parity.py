@@ -593,6 +593,51 @@ def test_graph_capture_of_the_dense_backward():
         assert_grad_loc(to_f64(gl), rgl, w.spatial_shapes)
 
 
+def test_concurrent_calls_from_host_threads():
+    """The library keeps no state between calls: four host threads, each with
+    its own stream and problem (dense and sparse grad_value routes), call the
+    forward and the backward at the same time; every result matches the oracle."""
+    import threading
+
+    wls = [encoder_workload(N=1, shapes=SMALL_LEVELS, M=8, D=32, K=4, seed=740 + i, with_grad=True)
+           if i % 2 == 0 else
+           decoder_workload(N=2, shapes=SMALL_LEVELS, Lq=30, dtype="f32", seed=740 + i, with_grad=True)
+           for i in range(4)]
+    refs = [(msda_forward(*_oracle_args(w)), msda_backward(*_oracle_args(w), w.grad_out)) for w in wls]
+    inputs = [device_inputs(w) for w in wls]
+    torch.cuda.synchronize()
+    results, errors = [None] * 4, []
+
+    def worker(i):
+        try:
+            value, loc, attn, grad_out = inputs[i]
+            w = wls[i]
+            s = torch.cuda.Stream()
+            with torch.cuda.stream(s):
+                for _ in range(3):
+                    out = msda.msda_forward(value, w.spatial_shapes, w.level_start, loc, attn)
+                    grads = msda.msda_backward(value, w.spatial_shapes, w.level_start, loc, attn, grad_out)
+            s.synchronize()
+            results[i] = (out, grads)
+        except Exception as e:  # reported by the main thread
+            errors.append((i, repr(e)))
+
+    note("concurrent calls: 4 host threads, own streams")
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(4)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    for i, w in enumerate(wls):
+        out, (gv, gl, ga) = results[i]
+        ref_out, (rgv, rgl, rga) = refs[i]
+        assert_f32("out", to_f64(out), ref_out)
+        assert_f32("grad_value", to_f64(gv), rgv)
+        assert_f32("grad_attn", to_f64(ga), rga)
+        assert_grad_loc(to_f64(gl), rgl, w.spatial_shapes)
+
+
 def test_batch_split_across_launches():
     """Images whose value slice exceeds 2^27 elements run one launch per image;
     every pointer (value, loc, attn, ref, outputs and gradients) is offset per
