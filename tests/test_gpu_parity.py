@@ -184,6 +184,26 @@ def test_channel_counts(D, dtype):
     assert_grad_loc(gl, rgl, w.spatial_shapes)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_single_pixel_levels(dtype):
+    """Levels of one pixel (its centre at normalised (0.5, 0.5)), beside a small
+    one: every sample inside interpolates towards the zero padding on both axes."""
+    w = uniform_workload(N=2, shapes=((1, 1), (2, 3), (1, 1)), Lq=37, M=3, D=8, K=5, dtype=dtype,
+                         seed=750, lo=-0.6, hi=1.6, with_grad=True)
+    note(f"single-pixel levels, {dtype}")
+    out = to_f64(gpu_forward(w))
+    ref = msda_forward(*_oracle_args(w))
+    if dtype == "f32":
+        assert_f32("out", out, ref)
+    else:
+        _check_bf16_out(out, ref)
+    gv, gl, ga = (to_f64(t) for t in gpu_backward(w))
+    rgv, rgl, rga = msda_backward(*_oracle_args(w), w.grad_out)
+    assert_f32("grad_value", gv, rgv)
+    assert_f32("grad_attn", ga, rga)
+    assert_grad_loc(gl, rgl, w.spatial_shapes)
+
+
 def test_max_levels_and_points():
     shapes = tuple((2 + (l % 5), 3 + (l % 4)) for l in range(16))
     w = uniform_workload(N=1, shapes=shapes, Lq=9, M=2, D=8, K=16, seed=200, with_grad=True)
