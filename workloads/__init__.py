@@ -22,6 +22,13 @@ is synthetic, with those shapes:
   samples of one (query, head), so they sum to 1 per head (section
   "Multi-scale deformable attention").
 
+The softmax and the reference-plus-offset locations above only draw the
+sampling core's inputs, following the workloads' stated recipe. The fused entry
+points (the step in front of the core) are instead given the raw draws (logits,
+reference points or boxes, offsets) from ``fused_workload``; the kernels and the
+oracle each form weights and locations from them on their own, and neither
+calls anything here to do so.
+
 Draw order with ``np.random.default_rng(seed)``: value -> reference points ->
 offsets -> logits -> grad_out. Values are drawn in float64 and cast to float32;
 bf16 values are float32 rounded to nearest-even and kept as raw uint16 bits,
