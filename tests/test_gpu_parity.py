@@ -295,6 +295,21 @@ def test_non_finite_locations_contribute_nothing(kind, dtype):
     assert not to_f64(gl).reshape(-1, 2)[pick].any() and not to_f64(ga).reshape(-1)[pick].any()
 
 
+def test_elongated_levels():
+    """A 1x20000 and a 20000x1 level: 2500 one-row (one-column) tiles each, so
+    the tiles are counted in global memory, coordinates reach 2e4, and 20000
+    queries of 8 samples keep the sorted grad_value route."""
+    w = uniform_workload(N=1, shapes=((1, 20000), (20000, 1)), Lq=20000, M=1, D=4, K=4, seed=760,
+                         with_grad=True)
+    note("elongated levels 1x20000 and 20000x1, dense backward")
+    assert_f32("out", to_f64(gpu_forward(w)), msda_forward(*_oracle_args(w)))
+    gv, gl, ga = (to_f64(t) for t in gpu_backward(w))
+    rgv, rgl, rga = msda_backward(*_oracle_args(w), w.grad_out)
+    assert_f32("grad_value", gv, rgv)
+    assert_f32("grad_attn", ga, rga)
+    assert_grad_loc(gl, rgl, w.spatial_shapes)
+
+
 def test_native_program_through_the_c_abi():
     """tests/c/abi_device.cpp (built with the library): plain HIP buffers and
     a stream of its own, no torch, forward and backward through the C ABI,
