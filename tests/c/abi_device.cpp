@@ -4,6 +4,7 @@
 // same channel vector c_m at every pixel, with weights summing to 1 per
 // (query, head) and every sample inside the map, out = c_m; grad_attn =
 // <grad_out, c_m>; grad_loc = 0; and <grad_out, out> = <grad_value, value>.
+// The two calls are then captured in a HIP graph and replayed (see below).
 // Prints one line per check and "OK" at the end; exit status 0 on success.
 #include <hip/hip_runtime.h>
 
@@ -110,6 +111,48 @@ int main() {
   std::printf("out vs c_m: %.3e\ngrad_attn vs <G, c_m>: %.3e\ngrad_loc vs 0: %.3e\nadjoint: %.3e\n", e_out, e_ga,
               e_gl, e_adj);
   fails += !(e_out <= 1e-6) + !(e_ga <= 1e-5) + !(e_gl <= 1e-4) + !(e_adj <= 1e-6);
+
+  // The same two calls captured into a HIP graph on this stream and replayed
+  // twice; before each replay the outputs are overwritten (eagerly, outside
+  // the graph) with NaN bytes. Every replay must reproduce the eager results:
+  // out, grad_loc and grad_attn bit for bit, grad_value to 1e-6.
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  HIP_OK(hipStreamBeginCapture(stream, hipStreamCaptureModeGlobal));
+  msda_status s1 = msda_forward(dv, &shapes[0][0], starts, dl, da, dout, N, S, M, D, L, Lq, K, MSDA_F32, stream);
+  msda_status s2 = msda_backward(dv, &shapes[0][0], starts, dl, da, dg, dgv, dgl, dga, N, S, M, D, L, Lq, K,
+                                 MSDA_F32, ws, ws_bytes, stream);
+  HIP_OK(hipStreamEndCapture(stream, &graph));
+  std::printf("captured forward: %s, backward: %s\n", msda_status_string(s1), msda_status_string(s2));
+  fails += (s1 != MSDA_SUCCESS) + (s2 != MSDA_SUCCESS);
+  HIP_OK(hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0));
+  for (int rep = 0; rep < 2; ++rep) {
+    HIP_OK(hipMemsetAsync(dout, 0xff, out.size() * 4, stream));
+    HIP_OK(hipMemsetAsync(dgv, 0xff, gv.size() * 4, stream));
+    HIP_OK(hipMemsetAsync(dgl, 0xff, gl.size() * 4, stream));
+    HIP_OK(hipMemsetAsync(dga, 0xff, ga.size() * 4, stream));
+    HIP_OK(hipStreamSynchronize(stream));
+    HIP_OK(hipGraphLaunch(exec, stream));
+    HIP_OK(hipStreamSynchronize(stream));
+    std::vector<float> out2(out.size()), gv2(gv.size()), gl2(gl.size()), ga2(ga.size());
+    HIP_OK(hipMemcpy(out2.data(), dout, out2.size() * 4, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(gv2.data(), dgv, gv2.size() * 4, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(gl2.data(), dgl, gl2.size() * 4, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(ga2.data(), dga, ga2.size() * 4, hipMemcpyDeviceToHost));
+    int diff = 0;
+    double e_gv = 0;
+    for (size_t i = 0; i < out.size(); ++i) diff += !(out2[i] == out[i]);
+    for (size_t i = 0; i < gl.size(); ++i) diff += !(gl2[i] == gl[i]);
+    for (size_t i = 0; i < ga.size(); ++i) diff += !(ga2[i] == ga[i]);
+    for (size_t i = 0; i < gv.size(); ++i) {
+      const double e = std::fabs((double)gv2[i] - (double)gv[i]);
+      e_gv = (e == e) ? std::fmax(e_gv, e) : INFINITY;  // NaN left behind counts as a failure
+    }
+    std::printf("graph replay %d: %d differing out/grad_loc/grad_attn elements, grad_value %.3e\n", rep, diff, e_gv);
+    fails += (diff != 0) + !(e_gv <= 1e-6);
+  }
+  HIP_OK(hipGraphExecDestroy(exec));
+  HIP_OK(hipGraphDestroy(graph));
 
   HIP_OK(hipFree(ws));
   for (float *p : {dv, dl, da, dout, dg, dgv, dgl, dga}) HIP_OK(hipFree(p));
