@@ -151,9 +151,9 @@ def _dims(value, loc, attn, grouped=False):
 
 
 def _device_tensor(t, what, dtype=None, device=None):
-    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise ValueError(f"{what} must be a device tensor")
-    if device is not None and t.device != device:
+    if device is not None and t.get_device() != device.index:
         raise ValueError(f"{what} is on {t.device}, value on {device}: all tensors of a call share one GPU")
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{what} must be {dtype}, got {t.dtype}")
@@ -176,18 +176,19 @@ def msda_forward(value, spatial_shapes, level_start, loc, attn, out=None, stream
     lib = load_library()
     _device_tensor(value, "value")
     dt = _dtype_code(value.dtype)
-    _device_tensor(loc, "loc", torch.float32, device=value.device)
-    _device_tensor(attn, "attn", torch.float32, device=value.device)
+    dev = value.device
+    _device_tensor(loc, "loc", torch.float32, device=dev)
+    _device_tensor(attn, "attn", torch.float32, device=dev)
     N, S, M, D, L, Lq, K = _dims(value, loc, attn)
     ss = _host_i64(spatial_shapes, (L, 2), "spatial_shapes")
     ls = _host_i64(level_start, (L,), "level_start")
     if out is None:
-        out = torch.empty((N, Lq, M, D), dtype=value.dtype, device=value.device)
+        out = torch.empty((N, Lq, M, D), dtype=value.dtype, device=dev)
     else:
-        _device_tensor(out, "out", value.dtype, device=value.device)
+        _device_tensor(out, "out", value.dtype, device=dev)
         if tuple(out.shape) != (N, Lq, M, D):
             raise ValueError(f"out must be {(N, Lq, M, D)}")
-    _raise(_call(value.device, stream, lib.msda_forward,
+    _raise(_call(dev, stream, lib.msda_forward,
             value.data_ptr(), ss.ctypes.data, ls.ctypes.data, loc.data_ptr(), attn.data_ptr(),
             out.data_ptr(), N, S, M, D, L, Lq, K, dt, writes=(out,)))
     return out
