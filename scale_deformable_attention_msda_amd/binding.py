@@ -459,3 +459,28 @@ class MSDeformAttnFused(torch.autograd.Function):
 def msda_fused_sample(value, spatial_shapes, level_start, ref, offsets, logits):
     """Differentiable sampling core fed by raw offsets and logits."""
     return MSDeformAttnFused.apply(value, spatial_shapes, level_start, ref, offsets, logits)
+
+
+class MSDeformAttnGrouped(torch.autograd.Function):
+    """Autograd wrapper of the deformable-group entry points (loc and attn per
+    group; value, loc and attn receive gradients)."""
+
+    @staticmethod
+    def forward(ctx, value, spatial_shapes, level_start, loc, attn):
+        ss = _host_i64(spatial_shapes, (loc.shape[3], 2), "spatial_shapes")
+        ls = _host_i64(level_start, (loc.shape[3],), "level_start")
+        ctx.save_for_backward(value, loc, attn)
+        ctx.levels = (ss, ls)
+        return msda_grouped_forward(value, ss, ls, loc, attn)
+
+    @staticmethod
+    def backward(ctx, grad_out):
+        value, loc, attn = ctx.saved_tensors
+        ss, ls = ctx.levels
+        gv, gl, ga = msda_grouped_backward(value, ss, ls, loc, attn, grad_out.contiguous())
+        return gv.to(value.dtype), None, None, gl, ga
+
+
+def msda_grouped_sample(value, spatial_shapes, level_start, loc, attn):
+    """Differentiable sampling core with deformable groups."""
+    return MSDeformAttnGrouped.apply(value, spatial_shapes, level_start, loc, attn)

@@ -123,3 +123,24 @@ def test_fused_inputs_with_groups(kind, ref_dim, G):
 
 def ss_sum(w):
     return np.maximum(w.spatial_shapes[:, 0], w.spatial_shapes[:, 1]).sum()
+
+
+def test_grouped_autograd_wrapper_matches_entry_points():
+    w = decoder_workload(N=2, shapes=((12, 20), (6, 10)), Lq=40, M=8, D=16, K=3, dtype="f32", seed=190,
+                         groups=2, with_grad=True)
+    value, loc, attn, g = device_inputs(w)
+    value.requires_grad_(True)
+    loc.requires_grad_(True)
+    attn.requires_grad_(True)
+    note("grouped autograd wrapper, G=2")
+    out = msda.msda_grouped_sample(value, w.spatial_shapes, w.level_start, loc, attn)
+    out.backward(g)
+    gv, gl, ga = msda.msda_grouped_backward(value.detach(), w.spatial_shapes, w.level_start, loc.detach(),
+                                            attn.detach(), g)
+    ref_out = msda.msda_grouped_forward(value.detach(), w.spatial_shapes, w.level_start, loc.detach(),
+                                        attn.detach())
+    torch.cuda.synchronize()
+    assert torch.equal(out.detach(), ref_out)
+    assert torch.allclose(value.grad, gv, atol=1e-6)
+    assert torch.equal(loc.grad, gl) and torch.equal(attn.grad, ga)
+    _check_out(w, to_f64(out.detach()), msda_grouped_forward(*_args(w)))
