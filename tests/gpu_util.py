@@ -132,3 +132,46 @@ def sample_rows(w, count, seed):
     s[: count // 4] = rng.integers(s0, d["S"], count // 4)
     n[-1], s[-1], m[-1] = d["N"] - 1, d["S"] - 1, d["M"] - 1
     return n, s, m
+
+
+# ---------------------------------------------------------------- fused inputs
+
+def fused_device_inputs(w, device="cuda:0"):
+    if w.dtype == "bf16":
+        value = torch.from_numpy(w.value_bits.view(np.int16).copy()).view(torch.bfloat16).to(device)
+    else:
+        value = torch.from_numpy(w.value).to(device)
+    ref = torch.from_numpy(w.ref).to(device)
+    off = torch.from_numpy(w.offsets).to(device)
+    logits = torch.from_numpy(w.logits).to(device)
+    g = None
+    if w.grad_out is not None:
+        if w.dtype == "bf16":
+            g = torch.from_numpy(w.grad_out_bits.view(np.int16).copy()).view(torch.bfloat16).to(device)
+        else:
+            g = torch.from_numpy(w.grad_out).to(device)
+    return value, ref, off, logits, g
+
+
+def fused_pixel_offsets(w, g_off, ref_rows):
+    """Offset gradients in pixel units of their level: points are already; boxes
+    are divided by (w * W_l, h * H_l). ref_rows: the reference rows [..., ref_dim]
+    matching g_off's leading axes."""
+    g_off = np.asarray(g_off, np.float64)
+    if w.ref.shape[-1] == 2:
+        return g_off
+    ss = w.spatial_shapes
+    size = np.stack([ss[:, 1], ss[:, 0]], axis=-1).reshape(-1, 1, 2).astype(np.float64)  # [L,1,2]
+    box = np.asarray(ref_rows, np.float64)[..., None, None, None, 2:]
+    return g_off / (size * box)
+
+
+def fused_ref_bound(w, off_rows):
+    """Per-element bound of grad_ref [..., ref_dim] for queries with offsets off_rows [..., M, L, K, 2]."""
+    ss = w.spatial_shapes
+    size = np.stack([ss[:, 1], ss[:, 0]], axis=-1).reshape(-1, 1, 2).astype(np.float64)  # (W_l, H_l)
+    off_rows = np.asarray(off_rows, np.float64)
+    centre = 1e-5 * np.broadcast_to(size, off_rows.shape).sum(axis=(-4, -3, -2))
+    if w.ref.shape[-1] == 2:
+        return centre
+    return np.concatenate([centre, 1e-5 * (size * np.abs(off_rows)).sum(axis=(-4, -3, -2))], axis=-1)

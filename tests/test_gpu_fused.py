@@ -16,30 +16,14 @@ torch = pytest.importorskip("torch")
 
 from oracle import msda_fused_backward, msda_fused_forward, msda_grad_value_rows  # noqa: E402
 from oracle import fused_locations, softmax_weights  # noqa: E402
-from tests.gpu_util import (assert_f32, assert_normwise, bf16_ulp, max_abs, note, to_f64)  # noqa: E402
+from tests.gpu_util import (assert_f32, assert_normwise, bf16_ulp, fused_device_inputs,  # noqa: E402
+                            fused_pixel_offsets, fused_ref_bound, max_abs, note, to_f64)
 import scale_deformable_attention_msda_amd as msda  # noqa: E402
 from workloads import COCO_LEVELS, fused_workload  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
 SMALL_LEVELS = ((20, 34), (10, 17), (5, 9), (3, 5))
-
-
-def _dev(w, device="cuda:0"):
-    if w.dtype == "bf16":
-        value = torch.from_numpy(w.value_bits.view(np.int16).copy()).view(torch.bfloat16).to(device)
-    else:
-        value = torch.from_numpy(w.value).to(device)
-    ref = torch.from_numpy(w.ref).to(device)
-    off = torch.from_numpy(w.offsets).to(device)
-    logits = torch.from_numpy(w.logits).to(device)
-    g = None
-    if w.grad_out is not None:
-        if w.dtype == "bf16":
-            g = torch.from_numpy(w.grad_out_bits.view(np.int16).copy()).view(torch.bfloat16).to(device)
-        else:
-            g = torch.from_numpy(w.grad_out).to(device)
-    return value, ref, off, logits, g
 
 
 def _oracle_args(w):
@@ -55,45 +39,21 @@ def _check_out(w, got, ref):
     assert not bad.any(), f"{bad.sum()} bf16 outputs beyond one ulp; worst {max_abs(got, ref):.3e}"
 
 
-def _pixel_offsets(w, g_off, ref_rows):
-    """Offset gradients in pixel units of their level: points are already; boxes
-    are divided by (w * W_l, h * H_l). ref_rows: the reference rows [..., ref_dim]
-    matching g_off's leading axes."""
-    g_off = np.asarray(g_off, np.float64)
-    if w.ref.shape[-1] == 2:
-        return g_off
-    ss = w.spatial_shapes
-    size = np.stack([ss[:, 1], ss[:, 0]], axis=-1).reshape(-1, 1, 2).astype(np.float64)  # [L,1,2]
-    box = np.asarray(ref_rows, np.float64)[..., None, None, None, 2:]
-    return g_off / (size * box)
-
-
-def _ref_bound(w, off_rows):
-    """Per-element bound of grad_ref [..., ref_dim] for queries with offsets off_rows [..., M, L, K, 2]."""
-    ss = w.spatial_shapes
-    size = np.stack([ss[:, 1], ss[:, 0]], axis=-1).reshape(-1, 1, 2).astype(np.float64)  # (W_l, H_l)
-    off_rows = np.asarray(off_rows, np.float64)
-    centre = 1e-5 * np.broadcast_to(size, off_rows.shape).sum(axis=(-4, -3, -2))
-    if w.ref.shape[-1] == 2:
-        return centre
-    return np.concatenate([centre, 1e-5 * (size * np.abs(off_rows)).sum(axis=(-4, -3, -2))], axis=-1)
-
-
 def _check_grads(w, got, ref, ref_rows, off_rows, check_gv=True):
     gv, go, gz, gr = got
     rgv, rgo, rgz, rgr = ref
     if check_gv:
         assert_f32("grad_value", gv, rgv)
     assert_f32("grad_logits", gz, rgz)
-    assert_f32("grad_offsets (pixel units)", _pixel_offsets(w, go, ref_rows), _pixel_offsets(w, rgo, ref_rows))
+    assert_f32("grad_offsets (pixel units)", fused_pixel_offsets(w, go, ref_rows), fused_pixel_offsets(w, rgo, ref_rows))
     if gr is not None:
         assert np.all(np.isfinite(gr)), "grad_ref: non-finite values"
-        excess = np.abs(np.asarray(gr, np.float64) - rgr) - _ref_bound(w, off_rows)
+        excess = np.abs(np.asarray(gr, np.float64) - rgr) - fused_ref_bound(w, off_rows)
         assert excess.max() <= 0, f"grad_ref beyond its bound by {excess.max():.3e}"
 
 
 def _gpu_fused_backward(w, **kw):
-    value, ref, off, logits, g = _dev(w)
+    value, ref, off, logits, g = fused_device_inputs(w)
     res = msda.msda_fused_backward(value, w.spatial_shapes, w.level_start, ref, off, logits, g, **kw)
     torch.cuda.synchronize()
     return tuple(None if t is None else to_f64(t) for t in res)
@@ -105,7 +65,7 @@ def _gpu_fused_backward(w, **kw):
 def test_fused_forward_encoder_small_maps_full(kind, ref_dim, dtype):
     w = fused_workload(kind, N=2, shapes=SMALL_LEVELS, ref_dim=ref_dim, dtype=dtype, seed=31)
     note(f"fused forward {kind} ref_dim={ref_dim} {dtype} small maps")
-    value, ref, off, logits, _ = _dev(w)
+    value, ref, off, logits, _ = fused_device_inputs(w)
     out = to_f64(msda.msda_fused_forward(value, w.spatial_shapes, w.level_start, ref, off, logits))
     torch.cuda.synchronize()
     _check_out(w, out, msda_fused_forward(*_oracle_args(w)))
@@ -115,7 +75,7 @@ def test_fused_forward_encoder_small_maps_full(kind, ref_dim, dtype):
 def test_fused_forward_decoder_full_config(ref_dim, dtype):
     w = fused_workload("decoder", N=2, Lq=300, ref_dim=ref_dim, dtype=dtype, seed=32 + ref_dim)
     note(f"fused forward decoder N=2 Lq=300 COCO levels ref_dim={ref_dim} {dtype}")
-    value, ref, off, logits, _ = _dev(w)
+    value, ref, off, logits, _ = fused_device_inputs(w)
     out = to_f64(msda.msda_fused_forward(value, w.spatial_shapes, w.level_start, ref, off, logits))
     torch.cuda.synchronize()
     _check_out(w, out, msda_fused_forward(*_oracle_args(w)))
@@ -151,7 +111,7 @@ def test_fused_hot_shapes_with_odd_point_counts(ref_dim, dtype):
     w = fused_workload("decoder", N=1, shapes=((24, 40), (12, 20), (6, 10)), Lq=5000, M=8, D=32, K=3,
                        ref_dim=ref_dim, dtype=dtype, seed=110 + ref_dim, with_grad=True)
     note(f"fused hot launch shapes with L*K=9, ref_dim={ref_dim}, {dtype}, 40000 pairs")
-    value, ref_t, off, logits, _ = _dev(w)
+    value, ref_t, off, logits, _ = fused_device_inputs(w)
     out = to_f64(msda.msda_fused_forward(value, w.spatial_shapes, w.level_start, ref_t, off, logits))
     _check_out(w, out, msda_fused_forward(*_oracle_args(w)))
     got = _gpu_fused_backward(w)
@@ -163,7 +123,7 @@ def test_fused_backward_encoder_full_size_sampled():
     w = fused_workload("encoder", N=2, shapes=COCO_LEVELS, K=4, seed=60, with_grad=True)
     d = w.dims
     note("fused backward encoder full size N=2 S=Lq=22223 M=8 D=32 K=4 f32")
-    value, ref, off, logits, g = _dev(w)
+    value, ref, off, logits, g = fused_device_inputs(w)
     gv, go, gz, gr = msda.msda_fused_backward(value, w.spatial_shapes, w.level_start, ref, off, logits, g)
     out = msda.msda_fused_forward(value, w.spatial_shapes, w.level_start, ref, off, logits)
     torch.cuda.synchronize()
@@ -213,7 +173,7 @@ def test_fused_shapes(L, K, D, dtype):
     w = fused_workload("decoder", N=1, shapes=shapes[:L], Lq=37, M=3, D=D, K=K, ref_dim=4 if L % 2 else 2,
                        dtype=dtype, seed=80 + L + K, with_grad=True)
     note(f"fused shapes L={L} K={K} D={D} {dtype}")
-    value, ref, off, logits, _ = _dev(w)
+    value, ref, off, logits, _ = fused_device_inputs(w)
     out = to_f64(msda.msda_fused_forward(value, w.spatial_shapes, w.level_start, ref, off, logits))
     torch.cuda.synchronize()
     _check_out(w, out, msda_fused_forward(*_oracle_args(w)))
@@ -225,7 +185,7 @@ def test_fused_nan_logit_poisons_only_its_head():
     w = fused_workload("decoder", N=1, shapes=((6, 8), (3, 4)), Lq=5, M=2, D=8, K=3, seed=90)
     w.logits[0, 2, 1, 0, 1] = np.nan
     note("fused forward with one NaN logit")
-    value, ref, off, logits, _ = _dev(w)
+    value, ref, off, logits, _ = fused_device_inputs(w)
     out = to_f64(msda.msda_fused_forward(value, w.spatial_shapes, w.level_start, ref, off, logits))
     torch.cuda.synchronize()
     ref_out = msda_fused_forward(*_oracle_args(w))
@@ -238,7 +198,7 @@ def test_fused_nan_logit_poisons_only_its_head():
 def test_fused_autograd_wrapper():
     w = fused_workload("decoder", N=1, shapes=((6, 8), (3, 4)), Lq=10, M=2, D=8, K=2, ref_dim=4, seed=95,
                        with_grad=True)
-    value, ref, off, logits, g = _dev(w)
+    value, ref, off, logits, g = fused_device_inputs(w)
     for t in (value, ref, off, logits):
         t.requires_grad_(True)
     note("fused autograd wrapper")

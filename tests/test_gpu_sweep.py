@@ -16,8 +16,8 @@ torch = pytest.importorskip("torch")
 from oracle import (msda_backward, msda_forward, msda_fused_backward, msda_fused_forward,  # noqa: E402
                     msda_grouped_backward, msda_grouped_forward)
 from tests.gpu_util import (assert_f32, assert_grad_loc, assert_normwise, bf16_ulp, device_inputs,  # noqa: E402
-                            gpu_backward, gpu_forward, max_abs, note, to_f64)
-from tests.test_gpu_fused import _dev, _pixel_offsets, _ref_bound  # noqa: E402
+                            fused_device_inputs, fused_pixel_offsets, fused_ref_bound, gpu_backward,
+                            gpu_forward, max_abs, note, to_f64)
 import scale_deformable_attention_msda_amd as msda  # noqa: E402
 from workloads import decoder_workload, fused_workload, uniform_workload  # noqa: E402
 
@@ -105,7 +105,7 @@ def test_random_fused_problem(case):
                        K=case["K"], dtype=case["dtype"], seed=case["seed"], ref_dim=case["ref_dim"],
                        groups=None if G == case["M"] else G, with_grad=True)
     note(f"fused sweep case {case}")
-    value, ref_t, off, logits, g = _dev(w)
+    value, ref_t, off, logits, g = fused_device_inputs(w)
     out = to_f64(msda.msda_fused_forward(value, w.spatial_shapes, w.level_start, ref_t, off, logits))
     gv, go, gz, gr = (to_f64(t) for t in msda.msda_fused_backward(value, w.spatial_shapes, w.level_start,
                                                                     ref_t, off, logits, g))
@@ -116,10 +116,10 @@ def test_random_fused_problem(case):
     heads = case["M"] // G
     assert_f32("grad_value", gv, rgv)
     assert_f32("grad_logits", gz, rgz, atol=1e-5 * heads)
-    assert_f32("grad_offsets (pixel units)", _pixel_offsets(w, go, w.ref), _pixel_offsets(w, rgo, w.ref),
+    assert_f32("grad_offsets (pixel units)", fused_pixel_offsets(w, go, w.ref), fused_pixel_offsets(w, rgo, w.ref),
                atol=1e-5 * heads)
     assert np.all(np.isfinite(gr))
-    excess = np.abs(gr - rgr) - heads * _ref_bound(w, w.offsets)
+    excess = np.abs(gr - rgr) - heads * fused_ref_bound(w, w.offsets)
     assert excess.max() <= 0, f"grad_ref beyond its bound by {excess.max():.3e}"
 
 
