@@ -300,16 +300,18 @@ def _round_sum_to_f32(a, b):
     Rounding the float64 sum to binary32 rounds twice; the two differ only when
     the float64 sum s is exactly halfway between two binary32 numbers while the
     exact sum is not. Knuth's TwoSum gives the exact error e = (a + b) - s, and
-    its sign then decides the halfway case."""
-    s = a + b
-    bv = s - a
-    e = (a - (s - bv)) + (b - bv)
-    r = s.astype(np.float32)
-    r64 = r.astype(np.float64)
-    other = np.where(r64 > s, np.nextafter(r, np.float32(-np.inf)), np.nextafter(r, np.float32(np.inf)))
-    halfway = (r64 + other.astype(np.float64)) * 0.5 == s
-    # at a halfway s, the exact sum lies on the side of `other` when e points there
-    toward_other = np.sign(e) == np.sign(other.astype(np.float64) - s)
+    its sign then decides the halfway case. A non-finite operand gives the
+    non-finite sum (its error term is NaN and the halfway test false)."""
+    with np.errstate(invalid="ignore"):
+        s = a + b
+        bv = s - a
+        e = (a - (s - bv)) + (b - bv)
+        r = s.astype(np.float32)
+        r64 = r.astype(np.float64)
+        other = np.where(r64 > s, np.nextafter(r, np.float32(-np.inf)), np.nextafter(r, np.float32(np.inf)))
+        halfway = (r64 + other.astype(np.float64)) * 0.5 == s
+        # at a halfway s, the exact sum lies on the side of `other` when e points there
+        toward_other = np.sign(e) == np.sign(other.astype(np.float64) - s)
     return np.where(halfway & (e != 0) & toward_other, other, r).astype(np.float32)
 
 
@@ -363,8 +365,13 @@ def msda_fused_backward(value, spatial_shapes, level_start, ref, offsets, logits
     else:
         wh = ref64[..., None, None, None, 2:]
         grad_off = gl * wh
+        # a sample outside the map (a non-finite location included, reading R2)
+        # is absent from the sum: its term is zero, not 0 * offset (NaN when the
+        # offset is infinite or NaN)
+        with np.errstate(invalid="ignore"):
+            size_terms = np.where(gl == 0.0, 0.0, gl * off)
         grad_ref = np.concatenate([gl.sum(axis=heads_levels_points),
-                                   (gl * off).sum(axis=heads_levels_points)], axis=-1)
+                                   size_terms.sum(axis=heads_levels_points)], axis=-1)
     return gv, grad_off, grad_logits, grad_ref
 
 

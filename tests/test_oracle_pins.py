@@ -521,6 +521,40 @@ def test_fused_backward_query_subset_agrees_with_full(ref_dim):
     np.testing.assert_allclose(gr_s, gr[qn, qq], rtol=0, atol=1e-12)
 
 
+@pytest.mark.parametrize("ref_dim", [2, 4])
+def test_fused_non_finite_offsets_act_as_far_outside(ref_dim):
+    """Reading R2 for formed locations: an offset that is NaN or infinite puts
+    its sample outside every level, so every result equals the one with that
+    offset replaced by a finite offset far outside the map (its weight still
+    enters the head's softmax); its own offset gradient is zero."""
+    rng = np.random.default_rng(111 + ref_dim)
+    shapes = np.array([[6, 8], [3, 5]])
+    starts = np.array([0, 48])
+    N, Lq, M, D, L, K = 2, 4, 2, 3, 2, 3
+    value = rng.standard_normal((N, 63, M, D))
+    ref = rng.uniform(0.3, 0.7, (N, Lq, ref_dim)).astype(np.float32)
+    if ref_dim == 4:
+        ref[..., 2:] = rng.uniform(0.1, 0.3, (N, Lq, 2))
+    off = (rng.standard_normal((N, Lq, M, L, K, 2)) * (1.5 if ref_dim == 2 else 0.3)).astype(np.float32)
+    logits = rng.standard_normal((N, Lq, M, L, K)).astype(np.float32)
+    G = rng.standard_normal((N, Lq, M, D))
+    bad, far = off.copy(), off.copy()
+    for (n, q, m, l, k, c), v in zip([(0, 1, 0, 0, 2, 0), (1, 3, 1, 1, 0, 1), (0, 0, 1, 1, 1, 0)],
+                                     [np.nan, np.inf, -np.inf]):
+        bad[n, q, m, l, k, c] = v
+        # far outside: 1e4 level pixels (points) or 1e4 box sizes (boxes) away
+        far[n, q, m, l, k, c] = 1e4 if v != -np.inf else -1e4
+    out_b = msda_fused_forward(value, shapes, starts, ref, bad, logits)
+    out_f = msda_fused_forward(value, shapes, starts, ref, far, logits)
+    np.testing.assert_array_equal(out_b, out_f)
+    res_b = msda_fused_backward(value, shapes, starts, ref, bad, logits, G)
+    res_f = msda_fused_backward(value, shapes, starts, ref, far, logits, G)
+    for a, b in zip(res_b, res_f):
+        assert np.all(np.isfinite(a))
+        np.testing.assert_array_equal(a, b)
+    assert res_b[1][0, 1, 0, 0, 2].tolist() == [0.0, 0.0]
+
+
 # --- deformable groups (reading R12) ---------------------------------------------------------
 
 def test_groups_of_one_head_are_the_core():
