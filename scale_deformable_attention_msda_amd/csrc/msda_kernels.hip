@@ -647,9 +647,12 @@ __device__ __forceinline__ void bwd_sample_body(const Params &p, int block, int 
             acc_rx += glx;
             acc_ry += gly;
             if (p.ref_dim == 4) {
+              // a sample outside the map (also one whose offset is not
+              // finite) has a zero location gradient and no term here,
+              // rather than 0 * offset
               const float2 o = soff[pp * dstride + g];
-              acc_bx = fmaf(glx, o.x, acc_bx);
-              acc_by = fmaf(gly, o.y, acc_by);
+              acc_bx = glx != 0.0f ? fmaf(glx, o.x, acc_bx) : acc_bx;
+              acc_by = gly != 0.0f ? fmaf(gly, o.y, acc_by) : acc_by;
             }
           }
         }

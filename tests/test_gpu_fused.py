@@ -195,6 +195,39 @@ def test_fused_nan_logit_poisons_only_its_head():
     assert_f32("out", out[keep], ref_out[keep])
 
 
+@pytest.mark.parametrize("ref_dim", [2, 4])
+def test_fused_non_finite_offsets(ref_dim):
+    """NaN and infinite offsets give non-finite locations, which lie outside
+    every level: those samples add nothing and get zero offset gradients, while
+    their weights still take part in the head's softmax (the oracle receives the
+    same offsets)."""
+    w = fused_workload("decoder", N=2, shapes=((12, 16), (6, 8)), Lq=30, M=4, D=8, K=3, ref_dim=ref_dim,
+                       seed=96 + ref_dim, with_grad=True)
+    rng = np.random.default_rng(97)
+    flat = w.offsets.reshape(-1, 2)
+    pick = rng.random(flat.shape[0]) < 0.15
+    bad = np.array([np.nan, np.inf, -np.inf], np.float32)
+    flat[pick, rng.integers(0, 2, size=int(pick.sum()))] = bad[rng.integers(0, 3, size=int(pick.sum()))]
+    note(f"fused forward and backward with non-finite offsets, ref_dim={ref_dim}")
+    value, ref_t, off, logits, g = fused_device_inputs(w)
+    out = to_f64(msda.msda_fused_forward(value, w.spatial_shapes, w.level_start, ref_t, off, logits))
+    gv, go, gz, gr = (to_f64(t) for t in msda.msda_fused_backward(value, w.spatial_shapes, w.level_start, ref_t,
+                                                                    off, logits, g))
+    torch.cuda.synchronize()
+    for t in (out, gv, go, gz, gr):
+        assert np.all(np.isfinite(t))
+    assert not go.reshape(-1, 2)[pick].any()
+    _check_out(w, out, msda_fused_forward(*_oracle_args(w)))
+    finite = np.isfinite(w.offsets).all(axis=-1, keepdims=True)
+    rgv, rgo, rgz, rgr = msda_fused_backward(*_oracle_args(w), w.grad_out)
+    assert_f32("grad_value", gv, rgv)
+    assert_f32("grad_logits", gz, rgz)
+    assert_f32("grad_offsets (pixel units)", fused_pixel_offsets(w, np.where(finite, go, 0.0), w.ref),
+               fused_pixel_offsets(w, np.where(finite, rgo, 0.0), w.ref))
+    excess = np.abs(gr - rgr) - fused_ref_bound(w, np.where(finite, w.offsets, 0.0))
+    assert excess.max() <= 0, f"grad_ref beyond its bound by {excess.max():.3e}"
+
+
 def test_fused_autograd_wrapper():
     w = fused_workload("decoder", N=1, shapes=((6, 8), (3, 4)), Lq=10, M=2, D=8, K=2, ref_dim=4, seed=95,
                        with_grad=True)
