@@ -183,6 +183,9 @@ msda_status msda_fused_forward(const void *value, const int64_t *spatial_shapes,
  *   grad_ref[n,q,:] = sum over (m, l, k) of grad_loc    (ref_dim 2)
  *                   = [sum grad_loc, sum grad_loc * offsets]  (ref_dim 4:
  *                     d/d(cx, cy), then d/d(w, h))
+ * A sample outside the map has zero grad_loc and no term in these sums, so a
+ * NaN or infinite offset (which puts its sample outside) leaves every result
+ * finite; its weight still takes part in its head's softmax.
  * grad_value [N,S,M,D], grad_offsets [N,Lq,M,L,K,2] (8-byte aligned),
  * grad_logits [N,Lq,M,L,K] and grad_ref [N,Lq,ref_dim] are float32 and
  * overwritten. grad_ref may be NULL (then it is not computed: reference
