@@ -48,5 +48,16 @@ def build_c_abi_check(source, exe):
     return exe
 
 
+def build_ceiling_probes(source, exe):
+    """Compile the hardware-ceiling probe program (plain HIP, no library)."""
+    cmd = [hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17",
+           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", source, "-o", exe + ".tmp"]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("ceiling probe build failed:\n" + " ".join(cmd) + "\n" + res.stderr)
+    os.replace(exe + ".tmp", exe)
+    return exe
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
