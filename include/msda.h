@@ -65,7 +65,8 @@ typedef enum msda_status {
   MSDA_ERROR_NOT_SUPPORTED = 2, /* L > 16, K > 16, D > 1024, oversized map, unknown dtype */
   MSDA_ERROR_MISALIGNED = 3,    /* a device pointer not aligned to its element size */
   MSDA_ERROR_LAUNCH = 4,        /* a kernel launch failed (HIP error after enqueue) */
-  MSDA_ERROR_WORKSPACE = 5      /* backward workspace missing or too small */
+  MSDA_ERROR_WORKSPACE = 5,     /* backward workspace missing or too small */
+  MSDA_ERROR_SCRATCH = 6        /* problem too large for the static scratch of msda_backward_static */
 } msda_status;
 
 typedef enum msda_dtype {
@@ -140,6 +141,30 @@ msda_status msda_backward(const void *value, const int64_t *spatial_shapes,
                           float *grad_attn, int64_t N, int64_t S, int64_t M, int64_t D,
                           int64_t L, int64_t Lq, int64_t K, int dtype, void *workspace,
                           size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * msda_backward for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results, determinism and asynchrony as msda_backward, with
+ * no workspace argument: the workspace is a static device array of
+ * MSDA_STATIC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends (its address is looked up once per device, on the
+ * first call with that device current). The call allocates and frees
+ * nothing. A problem whose msda_backward_workspace_size exceeds
+ * MSDA_STATIC_SCRATCH_BYTES returns MSDA_ERROR_SCRATCH before any HIP call
+ * (decoder-sized problems fit; an encoder-sized one, about 64 bytes per
+ * sample, does not). Every call on one GPU shares that GPU's array and the
+ * kernels clear what must start at zero, so consecutive calls need nothing
+ * from the caller; calls that overlap on one GPU (two streams or two host
+ * threads at once) race on the array and must not be issued.
+ */
+#define MSDA_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+
+msda_status msda_backward_static(const void *value, const int64_t *spatial_shapes,
+                                 const int64_t *level_start, const float *loc, const float *attn,
+                                 const void *grad_out, float *grad_value, float *grad_loc,
+                                 float *grad_attn, int64_t N, int64_t S, int64_t M, int64_t D,
+                                 int64_t L, int64_t Lq, int64_t K, int dtype, hipStream_t stream);
 
 /*
  * The sampling core with the step in front of it done inside the kernels

@@ -25,6 +25,7 @@ MSDA_ERROR_NOT_SUPPORTED = 2
 MSDA_ERROR_MISALIGNED = 3
 MSDA_ERROR_LAUNCH = 4
 MSDA_ERROR_WORKSPACE = 5
+MSDA_ERROR_SCRATCH = 6
 
 _lib = None
 
@@ -51,6 +52,8 @@ def load_library():
     lib.msda_forward.restype = ci
     lib.msda_backward.argtypes = [vp] * 9 + [i64] * 7 + [ci, vp, ctypes.c_size_t, vp]
     lib.msda_backward.restype = ci
+    lib.msda_backward_static.argtypes = [vp] * 9 + [i64] * 7 + [ci, vp]
+    lib.msda_backward_static.restype = ci
     lib.msda_backward_workspace_size.argtypes = [vp, vp] + [i64] * 7 + [ci, ctypes.POINTER(ctypes.c_size_t)]
     lib.msda_backward_workspace_size.restype = ci
     lib.msda_fused_forward.argtypes = [vp] * 4 + [ci] + [vp] * 3 + [i64] * 7 + [ci, vp]
@@ -255,6 +258,36 @@ def msda_backward(value, spatial_shapes, level_start, loc, attn, grad_out, grad_
             grad_out.data_ptr(), grad_value.data_ptr(), grad_loc.data_ptr(), grad_attn.data_ptr(), N, S, M,
             D, L, Lq, K, dt, workspace.data_ptr(), workspace.numel(),
             writes=(grad_value, grad_loc, grad_attn, workspace)))
+    return grad_value, grad_loc, grad_attn
+
+
+def msda_backward_static(value, spatial_shapes, level_start, loc, attn, grad_out, grad_value, grad_loc,
+                         grad_attn, stream=None):
+    """msda_backward without a workspace: the library's static per-GPU scratch
+    serves as one, so the call allocates nothing (the caller passes every
+    output). Raises MSDAError (status MSDA_ERROR_SCRATCH) when the problem
+    needs more than that scratch holds."""
+    lib = load_library()
+    _device_tensor(value, "value")
+    dt = _dtype_code(value.dtype)
+    dev = value.device
+    _device_tensor(loc, "loc", torch.float32, device=dev)
+    _device_tensor(attn, "attn", torch.float32, device=dev)
+    _device_tensor(grad_out, "grad_out", value.dtype, device=dev)
+    N, S, M, D, L, Lq, K = _dims(value, loc, attn)
+    ss = _host_i64(spatial_shapes, (L, 2), "spatial_shapes")
+    ls = _host_i64(level_start, (L,), "level_start")
+    for t, name, shape in ((grad_out, "grad_out", (N, Lq, M, D)), (grad_value, "grad_value", (N, S, M, D)),
+                           (grad_loc, "grad_loc", (N, Lq, M, L, K, 2)),
+                           (grad_attn, "grad_attn", (N, Lq, M, L, K))):
+        if name != "grad_out":
+            _device_tensor(t, name, torch.float32, device=dev)
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be {shape}")
+    _raise(_call(dev, stream, lib.msda_backward_static,
+            value.data_ptr(), ss.ctypes.data, ls.ctypes.data, loc.data_ptr(), attn.data_ptr(),
+            grad_out.data_ptr(), grad_value.data_ptr(), grad_loc.data_ptr(), grad_attn.data_ptr(), N, S, M,
+            D, L, Lq, K, dt, writes=(grad_value, grad_loc, grad_attn)))
     return grad_value, grad_loc, grad_attn
 
 

@@ -242,6 +242,21 @@ msda_status msda_backward(const void *value, const int64_t *spatial_shapes, cons
                        grad_attn, nullptr, N, S, M, D, L, Lq, K, dtype, workspace, workspace_bytes, stream);
 }
 
+msda_status msda_backward_static(const void *value, const int64_t *spatial_shapes, const int64_t *level_start,
+                                 const float *loc, const float *attn, const void *grad_out, float *grad_value,
+                                 float *grad_loc, float *grad_attn, int64_t N, int64_t S, int64_t M, int64_t D,
+                                 int64_t L, int64_t Lq, int64_t K, int dtype, hipStream_t stream) {
+  static_assert(msda::kStaticScratchBytes == MSDA_STATIC_SCRATCH_BYTES, "scratch size out of step with msda.h");
+  size_t need = 0;
+  msda_status st = msda_backward_workspace_size(spatial_shapes, level_start, N, S, M, D, L, Lq, K, dtype, &need);
+  if (st != MSDA_SUCCESS) return st;
+  if (need > msda::kStaticScratchBytes) return MSDA_ERROR_SCRATCH;
+  void *ws = nullptr;
+  if (msda::static_scratch(&ws) != hipSuccess) return MSDA_ERROR_LAUNCH;
+  return backward_impl(value, spatial_shapes, level_start, loc, attn, nullptr, 0, grad_out, grad_value, grad_loc,
+                       grad_attn, nullptr, N, S, M, D, L, Lq, K, dtype, ws, msda::kStaticScratchBytes, stream);
+}
+
 msda_status msda_fused_backward(const void *value, const int64_t *spatial_shapes, const int64_t *level_start,
                                 const float *ref, int ref_dim, const float *offsets, const float *logits,
                                 const void *grad_out, float *grad_value, float *grad_offsets, float *grad_logits,
@@ -299,6 +314,9 @@ const char *msda_status_string(msda_status status) {
     case MSDA_ERROR_MISALIGNED: return "MSDA_ERROR_MISALIGNED: a device pointer is not aligned to its element size";
     case MSDA_ERROR_LAUNCH: return "MSDA_ERROR_LAUNCH: a kernel launch failed";
     case MSDA_ERROR_WORKSPACE: return "MSDA_ERROR_WORKSPACE: workspace missing or smaller than msda_backward_workspace_size";
+    case MSDA_ERROR_SCRATCH:
+      return "MSDA_ERROR_SCRATCH: the problem needs more backward workspace than the static scratch "
+             "(MSDA_STATIC_SCRATCH_BYTES = 64 MiB) holds; use msda_backward with a workspace";
   }
   return "MSDA: unknown status";
 }

@@ -120,4 +120,11 @@ hipError_t launch_forward(const Params &p, DType dt, const LaunchShape &s, hipSt
 hipError_t launch_backward(const Params &p, DType dt, const LaunchShape &s, hipStream_t stream);
 hipError_t launch_zero(float *ptr, int64_t n, hipStream_t stream);
 
+// Bytes of the per-device static scratch array that the allocation-free
+// backward uses as its workspace (MSDA_STATIC_SCRATCH_BYTES in msda.h).
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+// Device address of the current device's scratch array (looked up once per
+// device, then cached).
+hipError_t static_scratch(void **ptr);
+
 }  // namespace msda

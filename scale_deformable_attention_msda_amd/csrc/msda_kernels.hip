@@ -29,6 +29,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "msda_internal.h"
@@ -1585,6 +1587,37 @@ hipError_t launch_backward(const Params &p_in, DType dt, const LaunchShape &s, h
     const int64_t n = p.pairs / p.M * p.ref_dim;
     return launch_fn(reinterpret_cast<const void *>(ref_grad_kernel), (n + kBlock - 1) / kBlock, kBlock, 1, p, stream);
   }
+  return hipSuccess;
+}
+
+// ------------------------------------------------- static backward scratch
+//
+// The workspace of the allocation-free backward entry point: one array per
+// GPU the library runs on, held until the process ends. Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in for
+// the symbol); it looks up the device address once per device with that
+// device current and passes that address, like a caller's workspace.
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(void **ptr) {
+  constexpr int kMaxDevices = 256;
+  static std::atomic<void *> addr[kMaxDevices];
+  static std::mutex mu;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void *p = addr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(mu);
+    p = addr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
   return hipSuccess;
 }
 

@@ -27,7 +27,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["msda_backward", "msda_backward_workspace_size", "msda_forward",
+    assert declared_functions() == ["msda_backward", "msda_backward_static", "msda_backward_workspace_size",
+                                    "msda_forward",
                                     "msda_fused_backward", "msda_fused_backward_workspace_size",
                                     "msda_fused_forward", "msda_grouped_backward",
                                     "msda_grouped_backward_workspace_size", "msda_grouped_forward",
@@ -41,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in range(6):
+    for code in range(7):
         s = msda.msda_status_string(code)
         assert s.startswith("MSDA_")
     assert "unknown" in msda.msda_status_string(99)
@@ -244,3 +245,21 @@ def test_header_compiles_as_c_and_links(tmp_path):
     run = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert run.returncode == 0, run.stdout + run.stderr
     assert run.stdout.strip().endswith("OK")
+
+
+def test_static_scratch_backward_rejects_oversized_problems_before_any_hip_call():
+    """The allocation-free backward checks the workspace it would need against its
+    static scratch on the host: an encoder-sized problem is refused with
+    MSDA_ERROR_SCRATCH (null device pointers are never touched), and a bad
+    argument still gets the ordinary validation status."""
+    lib = binding.load_library()
+    ss, ls = COCO.ctypes.data, STARTS.ctypes.data
+    st = lib.msda_backward_static(None, ss, ls, None, None, None, None, None, None,
+                                  1, 22223, 8, 32, 4, 22223, 4, 0, None)
+    assert st == binding.MSDA_ERROR_SCRATCH
+    assert "static scratch" in msda.msda_status_string(st)
+    need = msda.msda_backward_workspace_size(COCO, STARTS, 1, 22223, 8, 32, 4, 22223, 4)
+    assert need > (64 << 20)
+    st = lib.msda_backward_static(None, ss, ls, None, None, None, None, None, None,
+                                  1, 22223, 8, 32, 4, 22223, 17, 0, None)
+    assert st == binding.MSDA_ERROR_NOT_SUPPORTED  # K > 16
