@@ -102,6 +102,15 @@ def assert_normwise(name, got, ref, rtol=2e-2):
     return err
 
 
+def assert_bf16_out(got, ref):
+    """bf16 output: normwise bound, and within one bf16 ulp (+1e-5) elementwise,
+    since the float32 sum is rounded once to bf16."""
+    assert_normwise("out", got, ref)
+    slack = bf16_ulp(ref) + 1e-5
+    bad = np.abs(np.asarray(got, np.float64) - np.asarray(ref, np.float64)) > slack
+    assert not bad.any(), f"{bad.sum()} bf16 outputs beyond one ulp; worst {max_abs(got, ref):.3e}"
+
+
 def bf16_ulp(x):
     """Spacing of bfloat16 numbers at |x| (8 significant bits)."""
     x = np.abs(np.asarray(x, np.float64))

@@ -18,7 +18,7 @@ torch = pytest.importorskip("torch")
 
 from oracle import (fused_locations, msda_backward, msda_forward, msda_fused_backward,  # noqa: E402
                     msda_grad_value_rows, softmax_weights)
-from tests.gpu_util import (assert_f32, assert_grad_loc, assert_normwise, bf16_ulp,  # noqa: E402
+from tests.gpu_util import (assert_bf16_out, assert_f32, assert_grad_loc, assert_normwise, bf16_ulp,  # noqa: E402
                             device_inputs, gpu_backward, gpu_forward, max_abs, note, sample_pairs,
                             sample_rows, to_f64)
 import scale_deformable_attention_msda_amd as msda  # noqa: E402
@@ -37,11 +37,7 @@ def _oracle_args(w):
 
 
 def _check_bf16_out(got, ref):
-    assert_normwise("out", got, ref)
-    # one rounding of the fp32 sum to bf16: within one bf16 ulp of the exact result
-    slack = bf16_ulp(ref) + 1e-5
-    bad = np.abs(got - ref) > slack
-    assert not bad.any(), f"{bad.sum()} bf16 outputs beyond one ulp; worst {max_abs(got, ref):.3e}"
+    assert_bf16_out(got, ref)
 
 
 # ------------------------------------------------------------ full elementwise parity
