@@ -81,14 +81,6 @@ struct Params {
   int32_t seg_softmax;   // fused inputs: a pair's L*K logits sit in L*K consecutive lanes of
                          // the per-sample passes (L*K a power of two <= 64, one chunk)
   int32_t head_major;    // per-sample passes: a workgroup takes consecutive queries of one head
-  // Encoder-layout passes with value windows in LDS (every pixel a query,
-  // query q = value row q): workgroups take (head, image, pyramid tile), a
-  // tile being win_ty x win_tx pixels of level win_ref plus the pixels of the
-  // other levels whose centres fall inside it.
-  int32_t win_ref;       // finest level (tiling reference)
-  int32_t win_ty, win_tx;  // tile size in pixels of win_ref
-  int32_t win_ntx;       // tiles per row of win_ref
-  int32_t win_ntiles;    // tiles per (image, head)
   // Fused inputs (ref_dim 2 or 4): loc then holds offsets, attn holds logits,
   // and grad_loc / grad_attn receive the offset and logit gradients.
   // ref_dim 0: loc and attn are the sampling core's own inputs.

@@ -464,403 +464,6 @@ __global__ __launch_bounds__(kBlock) void fwd_kernel(const Params p) {
   }
 }
 
-// ------------------------------------------ forward with value windows in LDS
-//
-// Encoder queries are the pixels of the maps themselves (page "Deformable
-// DETR", section "Encoder": queries and keys are pixels of the multi-scale
-// maps and a query's reference point is its own pixel), so query q is value
-// row q, and queries that are near on the image sample overlapping
-// neighbourhoods at every level. A job is one pyramid tile (win_ty x win_tx
-// pixels of the finest level plus the pixels of every other level whose
-// centres fall inside that area) of one image and one head. A step is one
-// level of one job:
-//   geometry  read the step's sample locations and weights (one thread per
-//             sample), compute each sample's corner and weights once, and the
-//             bounding box of the corners the samples touch;
-//   stage     copy that box of the level's value rows of the head (the
-//             window; at most CAP rows; rows outside the map become zeros
-//             through the buffer range check) into LDS with direct
-//             global-to-LDS loads, and write each sample's descriptor (LDS
-//             offsets of its top and bottom corner rows, the four attention x
-//             bilinear weights);
-//   gather    read every sample's four corner rows from LDS and accumulate.
-// LDS serves random 128-byte rows at ~2.3x the L1 rate, and a window's rows
-// come from L2 once per step instead of once per corner. One workgroup per CU
-// works through a contiguous band of jobs with two window buffers: while it
-// gathers step s, the rows of step s + 1 are in flight into the other buffer
-// and the locations of step s + 2 into registers, so each step costs one
-// barrier and its memory latency is hidden behind the previous step's
-// gather. A window larger than CAP rows is cut to CAP rows around the
-// corners' mean; a sample with a corner outside it (an offset far beyond its
-// neighbours') reads its four rows from global memory instead. Correctness
-// does not depend on the layout, only the speed does. The weights and the
-// order of the sums are those of fwd_kernel, so both give the same bits.
-
-constexpr int kWinThreads = 512;   // one workgroup per CU
-constexpr int kWinRounds = 2;      // pair rounds per job
-constexpr int kWinBytes = 58 * 1024;  // one window buffer
-constexpr int kWinSamples = 640;   // sample descriptors per step (pairs x padded K)
-constexpr int kWinTiles = 8;       // tiles one workgroup's band of jobs may touch
-constexpr int kWinJobs = 256;      // jobs of one workgroup
-
-template <typename T, int LPP>
-struct WinCfg {
-  static constexpr int RB = LPP * 16;              // bytes of one head's row of value
-  static constexpr int VEC = 16 / T::size;         // elements per lane and row
-  static constexpr int PPR = kWinThreads / LPP;    // pairs per round
-  static constexpr int PMAX = kWinRounds * PPR;    // pairs per job (also bounded by kWinSamples / KP)
-  static constexpr int RPW = 64 / LPP;             // rows per wave staging instruction
-  static constexpr int CAP = kWinBytes / RB;       // window rows
-  static constexpr int ZERO = CAP + RPW;           // two rows of zeros, past the last staging overrun
-  static constexpr int ROWS = ZERO + 2;
-};
-
-// Descriptor mark of a sample with a corner outside the window (its rows are
-// read from global memory).
-constexpr uint32_t kWinGlobal = 0x80000000u;
-
-// Descriptor slots per pair: K rounded up to an odd count, so that the
-// descriptors of the pairs a wave reads at once sit on distinct banks.
-__host__ __device__ __forceinline__ int win_kp(int K) { return K | 1; }
-
-// First pixel (index along one axis, 0..n) of a level with n pixels whose
-// centre (x + 0.5) / n lies at or beyond the fraction a / r (32-bit: the
-// window path takes maps below 2^14 pixels a side).
-__host__ __device__ __forceinline__ int centre_from(int a, int n, int r) {
-  const int num = 2 * a * n - r, den = 2 * r;
-  const int c = num >= 0 ? (num + den - 1) / den : -((-num) / den);
-  return c < 0 ? 0 : (c > n ? n : c);
-}
-
-template <typename T, int LPP>
-__global__ __launch_bounds__(kWinThreads) void fwd_win_kernel(const Params p) {
-  using C = WinCfg<T, LPP>;
-  constexpr int RB = C::RB, VEC = C::VEC, PPR = C::PPR, RPW = C::RPW, CAP = C::CAP, PMAX = C::PMAX;
-  constexpr int NW = kWinThreads / 64;                                // waves
-  constexpr int SPT = (kWinSamples + kWinThreads - 1) / kWinThreads;  // samples per thread and step
-  __shared__ __align__(16) unsigned char win[2][C::ROWS * RB];
-  __shared__ __align__(16) float4 dw[2][kWinSamples];
-  __shared__ __align__(16) uint2 doff[2][kWinSamples];  // LDS offsets of the top and the bottom corner row
-  __shared__ uint32_t qlist[kWinTiles][PMAX];  // query index of each pair of a tile
-  __shared__ int32_t qcount[kWinTiles];
-  __shared__ int32_t rect[kWinTiles][kMaxLevels][4];  // per tile and query level: first x, first y, width, height
-  __shared__ uint32_t jobtab[kWinJobs];     // tile slot | image << 8 | head << 20
-  __shared__ __align__(16) int32_t wred[2][NW][4];  // per-wave corner box partials (read as int4)
-  __shared__ int32_t sH[kMaxLevels], sW[kMaxLevels], sS[kMaxLevels];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int L = p.L, K = p.K, KP = win_kp(K), LK = p.LK;
-  const int pmax = min(PMAX, kWinSamples / KP);  // the host sizes tiles to fit; this keeps LDS in bounds
-  // jobs: tile-major, then image, then head; the workgroups of an XCD (with the
-  // XCD-aware renumbering) take one contiguous band of them, so an XCD reads
-  // whole pixel rows (all heads) of one part of the image into its L2
-  const uint32_t nm = (uint32_t)(p.N * p.M);
-  const uint32_t njobs = (uint32_t)p.win_ntiles * nm;
-  const uint32_t lb = (uint32_t)xcd_remap(blockIdx.x, gridDim.x);
-  const uint32_t j0 = (uint32_t)(((uint64_t)njobs * lb) / gridDim.x);
-  const uint32_t j1 = (uint32_t)(((uint64_t)njobs * (lb + 1)) / gridDim.x);
-  const int nj = min((int)(j1 - j0), kWinJobs);  // the host keeps bands within kWinJobs
-  if (nj <= 0) return;
-  const uint32_t t0 = j0 / nm;
-  const int ntl = min((int)((j0 + nj - 1) / nm - t0) + 1, kWinTiles);  // and within kWinTiles tiles
-  const int S = nj * L;  // steps of this workgroup
-
-  // ---- setup: level table, zero rows, job table, every tile's pair list
-  if (tid < kMaxLevels) {
-    sH[tid] = tid < L ? p.lv.H[tid] : 1;
-    sW[tid] = tid < L ? p.lv.W[tid] : 1;
-    sS[tid] = tid < L ? p.lv.start[tid] : 0;
-  }
-  if (tid < 2 * 2 * RB / 16) {  // the zero rows of both buffers
-    const int b = tid / (2 * RB / 16), i = tid - b * (2 * RB / 16);
-    reinterpret_cast<float4 *>(win[b] + C::ZERO * RB)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-  }
-  for (int jj = tid; jj < nj; jj += kWinThreads) {
-    const uint32_t job = j0 + (uint32_t)jj;
-    const uint32_t t = job / nm, rem = job - t * nm;
-    const uint32_t n = rem / (uint32_t)p.M, m = rem - n * (uint32_t)p.M;
-    jobtab[jj] = (t - t0) | (n << 8) | (m << 20);
-  }
-  if (tid < ntl * L) {
-    const int ts = tid / L, lq = tid - ts * L;
-    const int t = (int)t0 + ts;
-    const int ty = t / p.win_ntx, tx = t - ty * p.win_ntx;
-    const int Wr = p.lv.W[p.win_ref], Hr = p.lv.H[p.win_ref];
-    const int X0 = tx * p.win_tx, X1 = min(X0 + p.win_tx, Wr);
-    const int Y0 = ty * p.win_ty, Y1 = min(Y0 + p.win_ty, Hr);
-    const int Wq = p.lv.W[lq], Hq = p.lv.H[lq];
-    const int xlo = centre_from(X0, Wq, Wr), ylo = centre_from(Y0, Hq, Hr);
-    rect[ts][lq][0] = xlo;
-    rect[ts][lq][1] = ylo;
-    rect[ts][lq][2] = max(0, centre_from(X1, Wq, Wr) - xlo);
-    rect[ts][lq][3] = max(0, centre_from(Y1, Hq, Hr) - ylo);
-  }
-  __syncthreads();
-  for (int ts = 0; ts < ntl; ++ts) {
-    // pair g of the tile: query levels in order, rows of each level's rectangle
-    int P = 0;
-    for (int lq = 0; lq < L; ++lq) {
-      const int xw = rect[ts][lq][2], cnt = xw * rect[ts][lq][3];
-      for (int g = tid - P; g < cnt; g += kWinThreads) {
-        if (g < 0) continue;
-        const int yy = g / xw, xx = g - yy * xw;
-        if (P + g < pmax) qlist[ts][P + g] = (uint32_t)(sS[lq] + (rect[ts][lq][1] + yy) * sW[lq] + rect[ts][lq][0] + xx);
-      }
-      P += cnt;
-    }
-    if (tid == 0) qcount[ts] = min(P, pmax);
-  }
-  __syncthreads();
-
-  // the registers of one step's samples in flight: location and weight
-  // (prefetch), then geometry
-  float2 pxy[SPT];
-  float pA[SPT];
-  int sx0[SPT], sy0[SPT];
-  float sa[SPT], sb[SPT], sA[SPT];
-  bool sin[SPT];
-  const uint32_t kmg = small_magic((uint32_t)K);
-
-  auto pair_of = [&](uint32_t jt, uint32_t q) {
-    return ((jt >> 8 & 0xfffu) * (uint32_t)p.Lq + q) * (uint32_t)p.M + (jt >> 20);
-  };
-
-  auto prefetch = [&](int jj, int l) {
-    const uint32_t jt = jobtab[jj];
-    const int ts = (int)(jt & 0xffu);
-    const int nsamp = qcount[ts] * K;
-#pragma unroll
-    for (int u = 0; u < SPT; ++u) {
-      const int i = tid + u * kWinThreads;
-      const bool ok = i < nsamp;
-      const int g = (int)small_div((uint32_t)(ok ? i : 0), kmg);
-      const int k = (ok ? i : 0) - g * K;
-      const uint32_t gi = pair_of(jt, qlist[ts][g]) * (uint32_t)LK + (uint32_t)(l * K + k);
-      pxy[u] = ok ? *reinterpret_cast<const float2 *>(p.loc + 2 * (size_t)gi) : make_float2(0.f, 0.f);
-      pA[u] = ok ? p.attn[gi] : 0.0f;
-    }
-  };
-
-  // geometry of a step from the prefetched registers; each wave's corner box
-  // goes to wred[b]
-  auto geometry = [&](int jj, int l, int b) {
-    const int nsamp = qcount[jobtab[jj] & 0xffu] * K;
-    const int H = sH[l], W = sW[l];
-    // empty-box sentinels that survive the float reduction exactly (map
-    // coordinates stay below 2^14)
-    int bx0 = 1 << 20, bx1 = -(1 << 20), by0 = 1 << 20, by1 = -(1 << 20);
-#pragma unroll
-    for (int u = 0; u < SPT; ++u) {
-      const bool ok = tid + u * kWinThreads < nsamp;
-      float x = fmaf(pxy[u].x, (float)W, -0.5f);
-      float y = fmaf(pxy[u].y, (float)H, -0.5f);
-      const bool inside = ok && (x >= -1.0f) && (x < (float)W) && (y >= -1.0f) && (y < (float)H);
-      x = inside ? x : 0.0f;
-      y = inside ? y : 0.0f;
-      const float xf = floorf(x), yf = floorf(y);
-      sa[u] = x - xf;
-      sb[u] = y - yf;
-      sA[u] = inside ? pA[u] : 0.0f;
-      sx0[u] = (int)xf;
-      sy0[u] = (int)yf;
-      sin[u] = inside;
-      if (inside) {
-        bx0 = min(bx0, sx0[u]);
-        bx1 = max(bx1, sx0[u]);
-        by0 = min(by0, sy0[u]);
-        by1 = max(by1, sy0[u]);
-      }
-    }
-    // the box of the wave (corners x0 .. x0 + 1, so the upper ends get +1 later)
-    bx0 = -(int)group_sum<64, true>(-(float)bx0, 64);
-    bx1 = (int)group_sum<64, true>((float)bx1, 64);
-    by0 = -(int)group_sum<64, true>(-(float)by0, 64);
-    by1 = (int)group_sum<64, true>((float)by1, 64);
-    if (lane == 0) *reinterpret_cast<int4 *>(wred[b][wave]) = make_int4(bx0, bx1, by0, by1);
-  };
-
-  // window of a step (from the partials in wred[b]), its staging into win[b],
-  // and the descriptors into dw / doff[b]
-  auto stage = [&](int jj, int l, int b) {
-    const uint32_t jt = jobtab[jj];
-    const uint32_t n = jt >> 8 & 0xfffu, m = jt >> 20;
-    const int H = sH[l], W = sW[l], s0 = sS[l];
-    int4 bx = *reinterpret_cast<const int4 *>(wred[b][0]);
-#pragma unroll
-    for (int w = 1; w < NW; ++w) {
-      const int4 o = *reinterpret_cast<const int4 *>(wred[b][w]);
-      bx = make_int4(min(bx.x, o.x), max(bx.y, o.y), min(bx.z, o.z), max(bx.w, o.w));
-    }
-    int wx0 = 0, wy0 = 0, ww = 0, wh = 0;
-    if (bx.x <= bx.y) {  // some sample of the step is inside the map
-      wx0 = bx.x;
-      wy0 = bx.z;
-      ww = bx.y + 2 - wx0;
-      wh = bx.w + 2 - wy0;
-      if (ww * wh > CAP) {
-        // cut to CAP rows around the box's centre
-        const float sc = sqrtf((float)CAP / ((float)ww * (float)wh));
-        int nw = max(2, min(ww, (int)((float)ww * sc)));
-        const int nh = max(2, min(wh, CAP / nw));
-        nw = max(1, min(ww, CAP / nh));
-        wx0 += (ww - nw) / 2;
-        wy0 += (wh - nh) / 2;
-        ww = nw;
-        wh = nh;
-      }
-    }
-    const int rows = ww * wh;
-    // staging: wave instruction k covers rows r0 .. r0 + RPW - 1 (lane / LPP),
-    // 16-byte piece lane % LPP of each; LDS destination win + r0 * RB + lane * 16
-    {
-      const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.value, p.value_elems * (uint32_t)T::size);
-      const uint32_t oob = kOobElem * (uint32_t)T::size;
-      const uint32_t wmg = small_magic((uint32_t)max(ww, 1));
-      const uint32_t rowb = (uint32_t)p.M * (uint32_t)RB;  // bytes between the rows of two pixels
-      const uint32_t base = (n * (uint32_t)p.S + (uint32_t)s0) * rowb + m * (uint32_t)RB + (uint32_t)(lane % LPP) * 16u;
-      for (int r0 = wave * RPW; r0 < rows; r0 += NW * RPW) {
-        const int r = r0 + lane / LPP;
-        const int wy = (int)small_div((uint32_t)r, wmg);
-        const int px = wx0 + r - wy * ww, py = wy0 + wy;
-        const bool inmap = r < rows && px >= 0 && px < W && py >= 0 && py < H;
-        const uint32_t goff = inmap ? base + (uint32_t)(py * W + px) * rowb : oob;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void *)(win[b] + r0 * RB),
-                                                 16, goff, 0, 0, 0);
-      }
-    }
-    const int nsamp = qcount[jt & 0xffu] * K;
-#pragma unroll
-    for (int u = 0; u < SPT; ++u) {
-      const int i = tid + u * kWinThreads;
-      if (i >= nsamp) continue;
-      const int g = (int)small_div((uint32_t)i, kmg);
-      const int slot = g * KP + (i - g * K);
-      const int x0 = sx0[u], y0 = sy0[u];
-      const float wa[2] = {1.0f - sa[u], sa[u]};
-      const float wb[2] = {1.0f - sb[u], sb[u]};
-      float wc[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int cy = y0 + (c >> 1), cx = x0 + (c & 1);
-        const bool ok = cy >= 0 && cy < H && cx >= 0 && cx < W;
-        wc[c] = ok ? sA[u] * wb[c >> 1] * wa[c & 1] : 0.0f;
-      }
-      dw[b][slot] = make_float4(wc[0], wc[1], wc[2], wc[3]);
-      const bool inwin = x0 >= wx0 && x0 + 1 < wx0 + ww && y0 >= wy0 && y0 + 1 < wy0 + wh;
-      const uint32_t top = (uint32_t)(((y0 - wy0) * ww + (x0 - wx0)) * RB);
-      const uint32_t zero = (uint32_t)(C::ZERO * RB);
-      // outside the map: zero weights on the zero rows (the same sums as the
-      // plain forward's zero weights on zero-padded rows). Outside the window:
-      // zero rows here, then the sample's rows from global memory
-      doff[b][slot] = !sin[u] ? make_uint2(zero, zero)
-                      : inwin ? make_uint2(top, top + (uint32_t)(ww * RB))
-                              : make_uint2(zero | kWinGlobal, zero);
-    }
-  };
-
-  const int gl = tid / LPP, j = tid - gl * LPP;
-  float acc[kWinRounds][VEC];
-#pragma unroll
-  for (int r = 0; r < kWinRounds; ++r)
-#pragma unroll
-    for (int e = 0; e < VEC; ++e) acc[r][e] = 0.0f;
-
-  // accumulate a step from win / dw / doff[b]; per pair, samples in order and
-  // corners in order (a sample outside the window adds its zero-row terms,
-  // exact no-ops, then its global rows)
-  auto gather = [&](int jj, int l, int b) {
-    const uint32_t jt = jobtab[jj];
-    const int ts = (int)(jt & 0xffu);
-    const int P = qcount[ts];
-    const unsigned char *wbuf = win[b];
-#pragma unroll
-    for (int r = 0; r < kWinRounds; ++r) {
-      if (r * PPR >= P) break;
-      const int g = min(r * PPR + gl, P - 1);  // lanes past the last pair repeat it (results unused)
-      for (int k = 0; k < K; ++k) {
-        const int slot = g * KP + k;
-        const uint2 o = doff[b][slot];
-        const float4 w4 = dw[b][slot];
-        const unsigned char *b0 = wbuf + (o.x & ~kWinGlobal) + j * 16;
-        const unsigned char *b1 = wbuf + o.y + j * 16;
-        const uint4 qs[4] = {*reinterpret_cast<const uint4 *>(b0), *reinterpret_cast<const uint4 *>(b0 + RB),
-                             *reinterpret_cast<const uint4 *>(b1), *reinterpret_cast<const uint4 *>(b1 + RB)};
-        const float wv[4] = {w4.x, w4.y, w4.z, w4.w};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const uint32_t wd[4] = {qs[c].x, qs[c].y, qs[c].z, qs[c].w};
-          float v[VEC];
-          if constexpr (std::is_same<T, F32>::value) {
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) v[e] = __uint_as_float(wd[e]);
-          } else {
-#pragma unroll
-            for (int e = 0; e < VEC / 2; ++e) {
-              v[2 * e] = __uint_as_float(wd[e] << 16);
-              v[2 * e + 1] = __uint_as_float(wd[e] & 0xffff0000u);
-            }
-          }
-#pragma unroll
-          for (int e = 0; e < VEC; ++e) acc[r][e] = fmaf(wv[c], v[e], acc[r][e]);
-        }
-        if (o.x & kWinGlobal) {
-          const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.value, p.value_elems * (uint32_t)T::size);
-          const uint32_t P2 = pair_of(jt, qlist[ts][g]);
-          const uint32_t gi = P2 * (uint32_t)LK + (uint32_t)(l * K + k);
-          const float2 xy = *reinterpret_cast<const float2 *>(p.loc + 2 * (size_t)gi);
-          const Sample sm = sample_geometry(p, pair_base(p, P2), xy, 1.0f, l, sH, sW, sS);
-          float vg[4][VEC];
-#pragma unroll
-          for (int c = 0; c < 4; ++c) load_vals<T, VEC>(rv, sm.off[c] * (uint32_t)T::size + (uint32_t)(j * 16), vg[c]);
-#pragma unroll
-          for (int c = 0; c < 4; ++c)
-#pragma unroll
-            for (int e = 0; e < VEC; ++e) acc[r][e] = fmaf(wv[c], vg[c][e], acc[r][e]);
-        }
-      }
-    }
-    if (l == L - 1) {
-#pragma unroll
-      for (int r = 0; r < kWinRounds; ++r) {
-        const int g = r * PPR + gl;
-        if (g < P) store_vals<T, VEC>(p.out, (int64_t)pair_of(jt, qlist[ts][g]) * p.D + j * VEC, acc[r]);
-#pragma unroll
-        for (int e = 0; e < VEC; ++e) acc[r][e] = 0.0f;
-      }
-    }
-  };
-
-  // ---- the pipeline over steps (job jj, level l), one barrier per step
-  prefetch(0, 0);
-  geometry(0, 0, 0);
-  int j1s = L > 1 ? 0 : 1, l1s = L > 1 ? 1 : 0;  // step 1
-  if (S > 1) prefetch(j1s, l1s);
-  __syncthreads();
-  stage(0, 0, 0);
-  int jjs = 0, ls = 0;  // step st
-  for (int st = 0; st < S; ++st) {
-    // step st + 2
-    int j2s = j1s, l2s = l1s + 1;
-    if (l2s == L) {
-      l2s = 0;
-      ++j2s;
-    }
-    // this thread's rows of step st have landed; the locations of step st + 1 too
-    __builtin_amdgcn_s_waitcnt(0);
-    if (st + 1 < S) geometry(j1s, l1s, (st + 1) & 1);
-    // every wave: rows of step st visible, box of step st + 1 complete, step
-    // st - 1 gathered (so its buffers are free)
-    __syncthreads();
-    if (st + 1 < S) stage(j1s, l1s, (st + 1) & 1);
-    if (st + 2 < S) prefetch(j2s, l2s);
-    gather(jjs, ls, st & 1);
-    jjs = j1s;
-    ls = l1s;
-    j1s = j2s;
-    l1s = l2s;
-  }
-}
-
 // --------------------------------------------------------------- backward
 //
 // The backward runs as a short pipeline on the caller's stream:
@@ -1893,95 +1496,8 @@ WorkspaceLayout workspace_layout(const int64_t *spatial_shapes, int64_t L, int64
   return w;
 }
 
-// Workgroups of the window forward: one per CU of the current device.
-int win_workgroups() {
-  static std::atomic<int> cached{0};
-  int cus = cached.load(std::memory_order_relaxed);
-  if (cus > 0) return cus;
-  int dev = 0, n = 0;
-  if (hipGetDevice(&dev) == hipSuccess &&
-      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
-    cus = n;
-  else
-    cus = 256;
-  cached.store(cus, std::memory_order_relaxed);
-  return cus;
-}
-
-// Tiling of the window forward for an encoder-layout launch: returns the
-// lanes per pair (4 or 8: one 16-byte piece of a 64- or 128-byte head row
-// each) and fills the win_* fields, or returns 0 when the launch does not
-// have that layout, row size or 16-byte alignment (the plain forward runs).
-int plan_window(Params &p, DType dt) {
-  if (p.ref_dim != 0 || p.Lq != p.S || p.L > kMaxLevels) return 0;
-  const int esz = dt == DType::F32 ? 4 : 2;
-  const int rb = p.D * esz;
-  const uintptr_t align = reinterpret_cast<uintptr_t>(p.value) | reinterpret_cast<uintptr_t>(p.out);
-  if ((rb != 64 && rb != 128) || (align & 15u) != 0) return 0;
-  int64_t covered = 0;
-  int ref = 0;
-  for (int l = 0; l < p.L; ++l) {
-    covered += (int64_t)p.lv.H[l] * p.lv.W[l];
-    if ((int64_t)p.lv.H[l] * p.lv.W[l] > (int64_t)p.lv.H[ref] * p.lv.W[ref]) ref = l;
-  }
-  if (covered != p.S) return 0;  // rows outside every level would be queries of no tile
-  for (int l = 0; l < p.L; ++l)
-    if (p.lv.H[l] >= (1 << 14) || p.lv.W[l] >= (1 << 14)) return 0;  // 32-bit tile arithmetic
-  if (p.N >= 4096 || p.M >= 4096) return 0;  // packed job table
-  const int lpp = rb / 16;
-  const int ppr = kWinThreads / lpp;
-  const int cap = kWinBytes / rb;
-  const int pmax = std::min(kWinRounds * ppr, kWinSamples / win_kp(p.K));
-  const int Wr = p.lv.W[ref], Hr = p.lv.H[ref];
-  auto from = [](int a, int n, int r) { return (int64_t)centre_from(a, n, r); };
-  // largest count of a level's pixels that one tile of size t along an axis
-  // of r reference pixels takes (per axis; the product bounds the tile's pairs)
-  auto widest = [&](int t, int r, int n) {
-    int64_t best = 0;
-    for (int a = 0; a < r; a += t) best = std::max(best, from(std::min(a + t, r), n, r) - from(a, n, r));
-    return best;
-  };
-  static const int kCand[][2] = {{16, 16}, {8, 16}, {16, 8}, {8, 8}, {4, 8}, {8, 4}, {4, 4}, {2, 4}, {4, 2},
-                                 {2, 2}, {1, 2}, {2, 1}, {1, 1}};
-  for (const auto &c : kCand) {
-    const int ty = std::min(c[0], Hr), tx = std::min(c[1], Wr);
-    // windows of an ordinary encoder tile (the tile plus about six pixels of
-    // offsets on each side) must fit
-    if ((ty + 12) * (tx + 12) > cap && !(ty == 1 && tx == 1)) continue;
-    int64_t bound = 0;
-    for (int l = 0; l < p.L; ++l) bound += widest(tx, Wr, p.lv.W[l]) * widest(ty, Hr, p.lv.H[l]);
-    if (bound > pmax) continue;
-    const int64_t ntx = (Wr + tx - 1) / tx, nty = (Hr + ty - 1) / ty;
-    const int64_t jobs = (int64_t)p.N * p.M * ntx * nty;
-    if (jobs > 0x7fffffff) return 0;
-    // a workgroup's band of jobs: at most kWinJobs of them over kWinTiles tiles
-    const int64_t grid = std::min<int64_t>(jobs, win_workgroups());
-    const int64_t per = (jobs + grid - 1) / grid;
-    if (per > kWinJobs || per / ((int64_t)p.N * p.M) + 2 > kWinTiles) return 0;
-    p.win_ref = ref;
-    p.win_ty = ty;
-    p.win_tx = tx;
-    p.win_ntx = (int32_t)ntx;
-    p.win_ntiles = (int32_t)(ntx * nty);
-    return lpp;
-  }
-  return 0;
-}
-
-hipError_t launch_forward(const Params &p_in, DType dt, const LaunchShape &s, hipStream_t stream) {
-  Params p = p_in;
-  const int lpp = plan_window(p, dt);
-  if (lpp == 0) return launch_pairs(true, p, dt, s, stream);
-  const void *fn;
-  if (dt == DType::F32)
-    fn = lpp == 8 ? reinterpret_cast<const void *>(fwd_win_kernel<F32, 8>)
-                  : reinterpret_cast<const void *>(fwd_win_kernel<F32, 4>);
-  else
-    fn = lpp == 4 ? reinterpret_cast<const void *>(fwd_win_kernel<BF16, 4>)
-                  : reinterpret_cast<const void *>(fwd_win_kernel<BF16, 8>);
-  // one workgroup per CU (the LDS of two window buffers), at most one per job
-  const int64_t jobs = (int64_t)p.N * p.M * p.win_ntiles;
-  return launch_fn(fn, std::min<int64_t>(jobs, win_workgroups()), kWinThreads, 1, p, stream);
+hipError_t launch_forward(const Params &p, DType dt, const LaunchShape &s, hipStream_t stream) {
+  return launch_pairs(true, p, dt, s, stream);
 }
 
 hipError_t launch_backward(const Params &p_in, DType dt, const LaunchShape &s, hipStream_t stream) {
