@@ -75,6 +75,18 @@ def traced_durations():
     return out or None
 
 
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (no GPU call)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, seconds):
     """The fp64 oracle, as it stands, on the first P (n, q, m) pairs of the same
     workload: forward plus backward (grad_value scatter included)."""
@@ -109,7 +121,7 @@ def cpu_baseline(w, seconds):
     return {"value": pts / t, "unit": "sampled points/s", "cores": 1, "kind": "oracle",
             "sample": f"{what} = {pts} points of the same workload, forward + "
                       f"backward in float64 NumPy, single-threaded ({t:.1f} s)",
-            "host_cpus_available": len(os.sched_getaffinity(0))}
+            "host_cpus_available": len(os.sched_getaffinity(0)), "cpu_model": cpu_model()}
 
 
 _POOL_WORKLOAD = None
@@ -168,7 +180,8 @@ def cpu_baseline_pool(w):
     pts = P * d["L"] * d["K"]
     return {"value": pts / wall, "unit": "sampled points/s", "cores": len(chunks), "kind": "oracle",
             "sample": f"first {P} (n,q,m) pairs = {pts} points, forward + backward, sharded over "
-                      f"{len(chunks)} spawned single-threaded workers ({wall:.1f} s wall)"}
+                      f"{len(chunks)} spawned single-threaded workers ({wall:.1f} s wall)",
+            "cpu_model": cpu_model()}
 
 
 def decoder_latency(msda, torch, dev, layers=6, reps=20):

@@ -1,8 +1,10 @@
 """Parity of the deformable-group entry points with the fp64 oracle, through
 the C ABI. Tolerances as for the sampling core: float32 max-abs <= 1e-5 (the
 location gradient in pixel units of its level), bf16 outputs within one bf16
-ulp. A group's location and weight gradients sum over its M/G heads, so their
-bound is M/G times the per-head one."""
+ulp. A group's location and weight gradients sum over its M/G heads and are
+still held to the per-head 1e-5 (their measured errors stay below it); only the
+reference gradient, a sum over a query's samples, takes the sum of their
+per-sample bounds."""
 import numpy as np
 import pytest
 
@@ -52,10 +54,9 @@ def test_grouped_backward_small_maps_full(G, K):
                                                                   attn, g))
     torch.cuda.synchronize()
     rgv, rgl, rga = msda_grouped_backward(*_args(w), w.grad_out)
-    heads = 8 // G
     assert_f32("grad_value", gv, rgv)
-    assert_f32("grad_attn", ga, rga, atol=1e-5 * heads)
-    assert_grad_loc(gl, rgl, w.spatial_shapes, atol=1e-5 * heads)
+    assert_f32("grad_attn", ga, rga, atol=1e-5)
+    assert_grad_loc(gl, rgl, w.spatial_shapes, atol=1e-5)
 
 
 @pytest.mark.parametrize("G,dtype", [(2, "bf16"), (1, "f32")])
@@ -69,10 +70,9 @@ def test_grouped_decoder_full_config(G, dtype):
     torch.cuda.synchronize()
     _check_out(w, out, msda_grouped_forward(*_args(w)))
     rgv, rgl, rga = msda_grouped_backward(*_args(w), w.grad_out)
-    heads = 8 // G
     assert_f32("grad_value", gv, rgv)
-    assert_f32("grad_attn", ga, rga, atol=1e-5 * heads)
-    assert_grad_loc(gl, rgl, w.spatial_shapes, atol=1e-5 * heads)
+    assert_f32("grad_attn", ga, rga, atol=1e-5)
+    assert_grad_loc(gl, rgl, w.spatial_shapes, atol=1e-5)
 
 
 def test_groups_equal_to_heads_match_the_core_bitwise():
@@ -108,14 +108,14 @@ def test_fused_inputs_with_groups(kind, ref_dim, G):
     rgv, rgo, rgz, rgr = msda_fused_backward(*args, w.grad_out)
     heads = 8 // G
     assert_f32("grad_value", gv, rgv)
-    assert_f32("grad_logits", gz, rgz, atol=1e-5 * heads)
+    assert_f32("grad_logits", gz, rgz, atol=1e-5)
     if ref_dim == 2:
-        assert_f32("grad_offsets", go, rgo, atol=1e-5 * heads)
+        assert_f32("grad_offsets", go, rgo, atol=1e-5)
     else:
         ss = w.spatial_shapes
         size = np.stack([ss[:, 1], ss[:, 0]], axis=-1).reshape(-1, 1, 2).astype(np.float64)
         box = w.ref.astype(np.float64)[:, :, None, None, None, 2:]
-        assert_f32("grad_offsets (pixel units)", go / (size * box), rgo / (size * box), atol=1e-5 * heads)
+        assert_f32("grad_offsets (pixel units)", go / (size * box), rgo / (size * box), atol=1e-5)
     # a query's reference gradient sums its G*L*K samples (bound: their pixel bounds in normalised units)
     bound = 1e-5 * heads * G * w.dims["K"] * float(ss_sum(w)) * (1 + (ref_dim == 4) * float(np.abs(w.offsets).max()))
     assert max_abs(gr, rgr) <= bound, (max_abs(gr, rgr), bound)

@@ -5,9 +5,9 @@ per-sample atomics and the tile sort, occur), float32 and bfloat16 values.
 Each case runs the forward and the backward and compares every output
 element, at the bars of the other parity tests. The same draw of sizes also
 drives the fused entry points (reference points or boxes, random deformable
-groups) and the grouped core; location, offset, logit and reference gradients
-of a group sum over its M/G heads, so their bounds are M/G times the per-head
-ones."""
+groups) and the grouped core; location, offset and logit gradients of a group
+sum over its M/G heads and are held to the per-head 1e-5; the reference
+gradient of a query sums all its samples and takes the sum of their bounds."""
 import numpy as np
 import pytest
 
@@ -115,9 +115,9 @@ def test_random_fused_problem(case):
     rgv, rgo, rgz, rgr = msda_fused_backward(*args, w.grad_out)
     heads = case["M"] // G
     assert_f32("grad_value", gv, rgv)
-    assert_f32("grad_logits", gz, rgz, atol=1e-5 * heads)
+    assert_f32("grad_logits", gz, rgz, atol=1e-5)
     assert_f32("grad_offsets (pixel units)", fused_pixel_offsets(w, go, w.ref), fused_pixel_offsets(w, rgo, w.ref),
-               atol=1e-5 * heads)
+               atol=1e-5)
     assert np.all(np.isfinite(gr))
     excess = np.abs(gr - rgr) - heads * fused_ref_bound(w, w.offsets)
     assert excess.max() <= 0, f"grad_ref beyond its bound by {excess.max():.3e}"
@@ -140,7 +140,6 @@ def test_random_grouped_problem(case):
     args = (w.value, w.spatial_shapes, w.level_start, w.loc, w.attn)
     _check_out(case["dtype"], out, msda_grouped_forward(*args))
     rgv, rgl, rga = msda_grouped_backward(*args, w.grad_out)
-    heads = case["M"] // G
     assert_f32("grad_value", gv, rgv)
-    assert_f32("grad_attn", ga, rga, atol=1e-5 * heads)
-    assert_grad_loc(gl, rgl, w.spatial_shapes, atol=1e-5 * heads)
+    assert_f32("grad_attn", ga, rga, atol=1e-5)
+    assert_grad_loc(gl, rgl, w.spatial_shapes, atol=1e-5)
