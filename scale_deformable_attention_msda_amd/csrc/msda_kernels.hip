@@ -154,15 +154,15 @@ __device__ __forceinline__ float group_sum(float v, int lpp_rt) {
   return v;
 }
 
+// Level table into LDS: thread l copies level l's entries (indexed reads of
+// the argument block, one per thread, rather than a chain of per-level
+// branches).
 __device__ __forceinline__ void load_levels(const Params &p, int32_t *sH, int32_t *sW, int32_t *sS) {
   const int tid = threadIdx.x;
-#pragma unroll
-  for (int l = 0; l < kMaxLevels; ++l) {
-    if (tid == l) {
-      sH[l] = p.lv.H[l];
-      sW[l] = p.lv.W[l];
-      sS[l] = p.lv.start[l];
-    }
+  if (tid < kMaxLevels) {
+    sH[tid] = p.lv.H[tid];
+    sW[tid] = p.lv.W[tid];
+    sS[tid] = p.lv.start[tid];
   }
 }
 
@@ -788,15 +788,12 @@ __device__ __forceinline__ bool sample_footprint(float lx, float ly, int H, int 
 __device__ __forceinline__ void load_tile_levels(const Params &p, int32_t *sH, int32_t *sW, int32_t *sS,
                                                  int32_t *sTW, int32_t *sToff) {
   const int tid = threadIdx.x;
-#pragma unroll
-  for (int l = 0; l < kMaxLevels; ++l) {
-    if (tid == l) {
-      sH[l] = p.lv.H[l];
-      sW[l] = p.lv.W[l];
-      sS[l] = p.lv.start[l];
-      sTW[l] = p.lv.TW[l];
-      sToff[l] = p.lv.toff[l];
-    }
+  if (tid < kMaxLevels) {
+    sH[tid] = p.lv.H[tid];
+    sW[tid] = p.lv.W[tid];
+    sS[tid] = p.lv.start[tid];
+    sTW[tid] = p.lv.TW[tid];
+    sToff[tid] = p.lv.toff[tid];
   }
 }
 
@@ -1078,7 +1075,7 @@ __device__ __forceinline__ void zero_split_body(const Params &p, int block, int 
 // with the coarse levels' crowded tiles) and one group of up to 64 channels
 // (blockIdx.y). The item's entries (at most kPartEntries = 4 per thread) are
 // read once; each corner that falls in the tile is bucketed by pixel with LDS
-// integer atomics into a (pair, weight) list; then thread (pixel, slice) sums
+// integer atomics into a (grad_out row, weight) list; then thread (pixel, slice) sums
 // its pixel's contributions to CS channels in registers, reading the grad_out
 // row slices straight from memory with several loads in flight.
 constexpr size_t kGvSmem = 4 * kPartEntries * sizeof(uint2) + (2 * kTilePix + 1) * 4 + 5 * kMaxLevels * 4;
@@ -1091,7 +1088,7 @@ constexpr size_t kGvSmem = 4 * kPartEntries * sizeof(uint2) + (2 * kTilePix + 1)
 // the buffer, which returns zeros; their weight is 0 too.
 template <typename T, int CS, bool VECP>
 __device__ __forceinline__ void gv_accumulate(const uint2 *lst, uint32_t jb, uint32_t je,
-                                              __amdgpu_buffer_rsrc_t ro, uint32_t D, uint32_t c0, int cnum,
+                                              __amdgpu_buffer_rsrc_t ro, uint32_t c0, int cnum,
                                               float (&acc)[CS]) {
   constexpr int VG = 16 / T::size;
   // entries in flight per thread (measured: 8 beats 4 up to 8 channels per
@@ -1107,11 +1104,13 @@ __device__ __forceinline__ void gv_accumulate(const uint2 *lst, uint32_t jb, uin
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       // read unconditionally (slots past je read the LDS words that follow
-      // the list, which the workgroup owns) so the reads issue together
-      const bool ok = j + u < je;
+      // the list, which the workgroup owns) so the reads issue together; an
+      // absent slot is masked bitwise rather than selected, so that the
+      // compiler cannot turn its read into a predicated one that waits alone
+      const uint32_t keep = j + u < je ? 0xffffffffu : 0u;
       const uint2 r2 = lst[j + u];
-      w[u] = ok ? __uint_as_float(r2.y) : 0.0f;
-      const uint32_t base = ok ? r2.x * D + c0 : kOobElem;
+      w[u] = __uint_as_float(r2.y & keep);
+      const uint32_t base = (r2.x & keep) + (keep ? c0 : kOobElem);
       if constexpr (VECP) {
 #pragma unroll
         for (int q = 0; q < CS / VG; ++q)
@@ -1135,7 +1134,7 @@ template <typename T, int CS>
 __device__ __forceinline__ void gv_body(const Params &p, uint32_t bx, int cgroup, unsigned char *smem) {
   constexpr int VG = 16 / T::size;  // elements of one 16-byte grad_out load
   constexpr int kEPT = kPartEntries / kBlock;  // entries per thread
-  uint2 *lst = reinterpret_cast<uint2 *>(smem);  // (pair, weight bits), pixel-major
+  uint2 *lst = reinterpret_cast<uint2 *>(smem);  // (grad_out row offset, weight bits), pixel-major
   uint32_t *cnt = reinterpret_cast<uint32_t *>(smem + 4 * kPartEntries * sizeof(uint2));
   uint32_t *off = cnt + kTilePix;
   int32_t *sH = reinterpret_cast<int32_t *>(off + kTilePix + 1);
@@ -1202,7 +1201,8 @@ __device__ __forceinline__ void gv_body(const Params &p, uint32_t bx, int cgroup
   for (int r = 0; r < kEPT; ++r)
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-      if (cin[r][c]) lst[off[cpix[r][c]] + crk[r][c]] = make_uint2(rec[r].x, __float_as_uint(cw[r][c]));
+      if (cin[r][c])
+        lst[off[cpix[r][c]] + crk[r][c]] = make_uint2(rec[r].x * (uint32_t)p.D, __float_as_uint(cw[r][c]));
   __syncthreads();
 
   const int c0 = cgroup * kChanGroup;
@@ -1224,12 +1224,12 @@ __device__ __forceinline__ void gv_body(const Params &p, uint32_t bx, int cgroup
   const uint32_t jb = off[pix], je = off[pix + 1];
   if constexpr (CS >= VG) {
     if (vec) {
-      gv_accumulate<T, CS, true>(lst, jb, je, ro, (uint32_t)p.D, (uint32_t)(c0 + slice * VG), CS, acc);
+      gv_accumulate<T, CS, true>(lst, jb, je, ro, (uint32_t)(c0 + slice * VG), CS, acc);
     } else {
-      gv_accumulate<T, CS, false>(lst, jb, je, ro, (uint32_t)p.D, (uint32_t)cbeg, cnum, acc);
+      gv_accumulate<T, CS, false>(lst, jb, je, ro, (uint32_t)cbeg, cnum, acc);
     }
   } else {
-    gv_accumulate<T, CS, false>(lst, jb, je, ro, (uint32_t)p.D, (uint32_t)cbeg, cnum, acc);
+    gv_accumulate<T, CS, false>(lst, jb, je, ro, (uint32_t)cbeg, cnum, acc);
   }
 
   const int64_t row0 = (int64_t)n * p.S + sS[l];
