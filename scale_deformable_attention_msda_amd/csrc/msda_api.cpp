@@ -132,6 +132,10 @@ msda_status backward_impl(const void *value, const int64_t *spatial_shapes, cons
   p.ws.n_work = reinterpret_cast<uint32_t *>(ws + wl.off_nwork);
   p.ws.split_list = reinterpret_cast<uint32_t *>(ws + wl.off_split);
   p.ws.entries = reinterpret_cast<uint32_t *>(ws + wl.off_entries);
+  {
+    const uint64_t eb = 16 * (uint64_t)wl.Emax;  // the region the scatter pass writes
+    p.ws.entries_bytes = eb <= msda::kEntriesOob ? (uint32_t)eb : 0u;
+  }
   p.ws.ref_part = reinterpret_cast<float *>(ws + wl.off_refpart);
   p.ws.floc = reinterpret_cast<float *>(ws + wl.off_floc);
   p.ws.fattn = reinterpret_cast<float *>(ws + wl.off_fattn);

@@ -20,6 +20,10 @@ constexpr uint32_t kOobElem = 1u << 28;
 constexpr int64_t kMaxSliceElems = (int64_t)kOobElem - 1;
 // Samples (N*Lq*M*L*K) of one launch must have 32-bit indices.
 constexpr int64_t kMaxSliceSamples = (int64_t)1 << 31;
+// Byte offset that marks an absent sort entry in the scatter pass's buffer
+// stores: at or past the end of any entries region whose size is below it
+// (a larger region uses plain stores instead).
+constexpr uint32_t kEntriesOob = 0xfffffff0u;
 
 // grad_value is produced per 8x8-pixel tile of each (image, head, level).
 constexpr int kTile = 8;
@@ -49,6 +53,7 @@ struct Workspace {
   uint32_t *n_work;       // [1]
   uint32_t *split_list;   // [T] tiles whose entries span several work items
   uint32_t *entries;      // [4*Emax] (sample, tile) entries, tile-major, 16-byte records
+  uint32_t entries_bytes; // bytes of the entries region when below kEntriesOob (buffer stores), else 0
   float *ref_part;        // [4*pairs] per-pair sums of the reference gradient (fused inputs)
   float *floc;            // [2*samples] locations formed from the fused inputs
   float *fattn;           // [samples] weights formed from the fused inputs

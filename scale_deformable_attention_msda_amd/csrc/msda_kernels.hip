@@ -809,10 +809,13 @@ __device__ __forceinline__ void zero_split_body(const Params &p, int block, int 
                                                 const int32_t *sW, const int32_t *sS, const int32_t *sTW,
                                                 const int32_t *sToff);
 
-template <int MODE>
+// LOCAL: a (image, head)'s tiles fit the LDS histogram (TPI <= kBinCap),
+// otherwise every entry goes to the global counters; the two are separate
+// instantiations so that neither path's waits fall into the other.
+template <int MODE, bool LOCAL>
 __global__ __launch_bounds__(kBlock) void bin_kernel(const Params p) {
-  __shared__ uint32_t cnt[kBinCap];
-  __shared__ uint32_t gbase[MODE == 1 ? kBinCap : 1];
+  __shared__ uint32_t cnt[LOCAL ? kBinCap : 1];
+  __shared__ uint32_t gbase[MODE == 1 && LOCAL ? kBinCap : 1];
   __shared__ int32_t sH[kMaxLevels], sW[kMaxLevels], sS[kMaxLevels], sTW[kMaxLevels], sToff[kMaxLevels];
   load_tile_levels(p, sH, sW, sS, sTW, sToff);
   const int tid = threadIdx.x;
@@ -835,7 +838,7 @@ __global__ __launch_bounds__(kBlock) void bin_kernel(const Params p) {
   const int q0 = qb * qpb;
   const int nsamp = (min(p.Lq, q0 + qpb) - q0) * p.LK;
   const uint32_t tbase = ((uint32_t)m * (uint32_t)p.N + (uint32_t)n) * (uint32_t)p.TPI;
-  const bool local = p.TPI <= kBinCap;
+  constexpr bool local = LOCAL;
   uint4 *rec_out = reinterpret_cast<uint4 *>(p.ws.entries);
   if (local)
     for (int i = tid; i < p.TPI; i += kBlock) cnt[i] = 0;
@@ -864,7 +867,11 @@ __global__ __launch_bounds__(kBlock) void bin_kernel(const Params p) {
 #pragma unroll
   for (int r = 0; r < NS; ++r) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) has[r][k] = false;
+    for (int k = 0; k < 4; ++k) {
+      has[r][k] = false;
+      tl[r][k] = 0;
+      rk[r][k] = 0;
+    }
     const int i = tid + r * kBlock;
     if (i >= nsamp) continue;
     const int qi = (int)small_div((uint32_t)i, lkmg);
@@ -909,16 +916,37 @@ __global__ __launch_bounds__(kBlock) void bin_kernel(const Params p) {
     }
   } else {
     // reserve each tile's run once per workgroup, then write the records
+    // (every slot's run start read first, unconditionally, so that the reads
+    // issue together instead of one wait per record)
     for (int i = tid; i < p.TPI; i += kBlock) {
       const uint32_t c = cnt[i];
       if (c) gbase[i] = atomicAdd(p.ws.tile_cursor + tbase + i, c);
     }
     __syncthreads();
+    uint32_t dst[NS][4];
 #pragma unroll
     for (int r = 0; r < NS; ++r)
 #pragma unroll
-      for (int k = 0; k < 4; ++k)
-        if (has[r][k]) rec_out[gbase[tl[r][k]] + rk[r][k]] = rec[r];
+      for (int k = 0; k < 4; ++k) dst[r][k] = gbase[has[r][k] ? tl[r][k] : 0u] + rk[r][k];
+    if (p.ws.entries_bytes != 0) {
+      // buffer stores with 32-bit offsets, issued back to back; an absent
+      // slot's offset lies past the entries region (whose size the resource
+      // carries), so the hardware drops that store
+      const __amdgpu_buffer_rsrc_t rr = make_rsrc(rec_out, p.ws.entries_bytes);
+#pragma unroll
+      for (int r = 0; r < NS; ++r) {
+        const u32x4 d = {rec[r].x, rec[r].y, rec[r].z, rec[r].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          __builtin_amdgcn_raw_buffer_store_b128(d, rr, has[r][k] ? dst[r][k] * 16u : kEntriesOob, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < NS; ++r)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (has[r][k]) rec_out[dst[r][k]] = rec[r];
+    }
   }
 }
 
@@ -1546,8 +1574,11 @@ hipError_t launch_backward(const Params &p_in, DType dt, const LaunchShape &s, h
     //    the tiles whose grad_value is summed over several work items
     const int64_t bin_blocks = (int64_t)p.N * p.M * ((p.Lq + p.qpb - 1) / p.qpb);
     const int64_t bin0_blocks = (int64_t)p.N * p.M * ((p.Lq + p.qpb0 - 1) / p.qpb0);
-    const void *bin0 = reinterpret_cast<const void *>(bin_kernel<0>);
-    const void *bin1 = reinterpret_cast<const void *>(bin_kernel<1>);
+    const bool local = p.TPI <= kBinCap;
+    const void *bin0 = local ? reinterpret_cast<const void *>(bin_kernel<0, true>)
+                             : reinterpret_cast<const void *>(bin_kernel<0, false>);
+    const void *bin1 = local ? reinterpret_cast<const void *>(bin_kernel<1, true>)
+                             : reinterpret_cast<const void *>(bin_kernel<1, false>);
     if ((e = launch_fn(bin0, bin0_blocks, kBlock, 1, p, stream)) != hipSuccess) return e;
     if ((e = launch_fn(reinterpret_cast<const void *>(scan_kernel), 1, 1024, 1, p, stream)) != hipSuccess) return e;
     if ((e = launch_fn(bin1, bin_blocks + 256, kBlock, 1, p, stream)) != hipSuccess) return e;
