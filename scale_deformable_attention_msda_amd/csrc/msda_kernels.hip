@@ -665,7 +665,7 @@ __device__ __forceinline__ void bwd_sample_body(const Params &p, int block, int 
     }
     __syncthreads();
     for (int i = tid; i < npairs * pcn; i += kBlock) {
-      const int gg = i / pcn;
+      const int gg = (int)small_div((uint32_t)i, pmg);
       const int pp = i - gg * pcn;
       const float3 r = res[pp * dstride + gg];
       const int64_t gi = pr(gg) * p.LK + pc0 + pp;
@@ -1187,7 +1187,13 @@ __device__ __forceinline__ void gv_body(const Params &p, uint32_t bx, int cgroup
   __syncthreads();
   int n, m, l, ty, tx;
   decode_tile(p, t, sToff, sTW, n, m, l, ty, tx);
-  const int H = sH[l], W = sW[l];
+  // the item's tile and level are uniform: scalar registers, so that the
+  // per-corner tests below wait on nothing (LDS-loaded values would make the
+  // compiler wait for every LDS atomic issued since)
+  l = __builtin_amdgcn_readfirstlane(l);
+  ty = __builtin_amdgcn_readfirstlane(ty);
+  tx = __builtin_amdgcn_readfirstlane(tx);
+  const int H = __builtin_amdgcn_readfirstlane(sH[l]), W = __builtin_amdgcn_readfirstlane(sW[l]);
 
   // corners of this thread's entries that fall in the tile, ranked per pixel
   uint32_t cpix[kEPT][4], crk[kEPT][4];
