@@ -13,9 +13,9 @@ image n, query q and head m,
 
 where x^l_m(.) reads level l of head m's value map at a fractional location by
 bilinear interpolation of the four surrounding pixels (same page, section
-"Deformable attention module", symbol list; page "Deformable Attention Module",
-"bilinear interpolation is applied as in Dai et al. (2017)"; page "Deformable
-Attention", bilinear from the four nearest pixels). The library receives the
+"Deformable attention module", symbol list; page "Deformable Attention
+Module", its definition of the module: the bilinear sampling follows Dai et
+al. 2017; page "Deformable Attention", bilinear from the four nearest pixels). The library receives the
 sampling location already formed, as normalised coordinates
 loc = phi_l-normalised reference + offset, so loc[...,0] is x (width) and
 loc[...,1] is y (height), both in [0,1] inside the image.
