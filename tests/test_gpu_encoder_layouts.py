@@ -65,3 +65,20 @@ def test_level_order_and_tiny_levels():
 def test_channel_counts_and_points(D, dtype):
     _check(encoder_workload(N=1, shapes=SMALL_LEVELS, M=4, D=D, K=8 if D == 32 else 4, dtype=dtype, seed=1206),
            f"D={D}")
+
+
+def test_three_image_launch_matches_per_image_launches():
+    """Three mid-sized encoder images in one fp32 launch (6120 workgroups; with
+    the extra query of _check, a ragged last workgroup) against the oracle, and
+    bit for bit against each image launched on its own (2040 workgroups): a
+    query's result does not depend on the batch it is launched with."""
+    w = encoder_workload(N=3, shapes=MID_LEVELS, M=8, D=32, K=4, seed=1207)
+    _check(w, "three images in one launch")
+    value, loc, attn, _ = device_inputs(w)
+    ss, ls = w.spatial_shapes, w.level_start
+    out = msda.msda_forward(value, ss, ls, loc, attn)
+    singles = [msda.msda_forward(value[n:n + 1].contiguous(), ss, ls, loc[n:n + 1].contiguous(),
+                                 attn[n:n + 1].contiguous()) for n in range(3)]
+    torch.cuda.synchronize()
+    for n in range(3):
+        assert torch.equal(out[n:n + 1], singles[n]), f"image {n}"
