@@ -86,6 +86,8 @@ struct Params {
   int32_t seg_softmax;   // fused inputs: a pair's L*K logits sit in L*K consecutive lanes of
                          // the per-sample passes (L*K a power of two <= 64, one chunk)
   int32_t head_major;    // per-sample passes: a workgroup takes consecutive queries of one head
+  int32_t form_inputs;   // fused inputs: the counting pass forms every sample's location and
+                         // weight from the raw inputs and stores them in the workspace
   // Fused inputs (ref_dim 2 or 4): loc then holds offsets, attn holds logits,
   // and grad_loc / grad_attn receive the offset and logit gradients.
   // ref_dim 0: loc and attn are the sampling core's own inputs.

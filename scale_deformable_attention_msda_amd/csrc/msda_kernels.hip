@@ -847,6 +847,9 @@ __global__ __launch_bounds__(kBlock) void bin_kernel(const Params p) {
   // The thread's samples: all their loads first (one round trip), then
   // the tile walk. Sample i is (query qi = i / LK, point pt = i % LK).
   const uint32_t lkmg = small_magic((uint32_t)p.LK), kmg = small_magic((uint32_t)p.K);
+  // fused inputs formed here: the raw offsets and logits are read instead
+  // (L*K a power of two <= 64, so a pair's samples are L*K aligned lanes)
+  const bool form = MODE == 0 && p.form_inputs != 0;
   float2 xyv[NS];
   float av[NS];
 #pragma unroll
@@ -856,8 +859,28 @@ __global__ __launch_bounds__(kBlock) void bin_kernel(const Params p) {
     const int qi = (int)small_div((uint32_t)(ok ? i : 0), lkmg);
     const int pt = (ok ? i : 0) - qi * p.LK;
     const int64_t sid = (((int64_t)n * p.Lq + q0 + qi) * p.M + m) * p.LK + pt;
-    xyv[r] = ok ? *reinterpret_cast<const float2 *>(p.loc + 2 * sid) : make_float2(0.0f, 0.0f);
-    av[r] = MODE == 1 && ok ? p.attn[sid] : 0.0f;
+    xyv[r] = ok ? *reinterpret_cast<const float2 *>((form ? p.offsets : p.loc) + 2 * sid) : make_float2(0.0f, 0.0f);
+    av[r] = (MODE == 1 || form) && ok ? (form ? p.logits : p.attn)[sid] : 0.0f;
+  }
+  if (form) {
+    // each sample's location and softmax weight, as fused_inputs_kernel forms
+    // them (the same functions, the same lane positions within a pair's
+    // segment), stored for the passes that follow
+#pragma unroll
+    for (int r = 0; r < NS; ++r) {
+      const int i = tid + r * kBlock;
+      const bool ok = i < nsamp;  // whole pairs drop out together
+      const float A = segment_softmax(av[r], p.LK);
+      if (!ok) continue;
+      const int qi = (int)small_div((uint32_t)i, lkmg);
+      const int pt = i - qi * p.LK;
+      const int l = (int)small_div((uint32_t)pt, kmg);
+      const int64_t q = (int64_t)n * p.Lq + q0 + qi;
+      const int64_t sid = (q * p.M + m) * p.LK + pt;
+      xyv[r] = form_loc<true>(p, xyv[r], l, load_ref(p, (uint32_t)q), sH, sW);
+      *reinterpret_cast<float2 *>(p.ws.floc + 2 * sid) = xyv[r];
+      p.ws.fattn[sid] = A;
+    }
   }
   // Up to four tiles per sample, in fixed slots (dy, dx) so that every array
   // index below is a compile-time constant.
@@ -1541,9 +1564,16 @@ hipError_t launch_backward(const Params &p_in, DType dt, const LaunchShape &s, h
   set_sample_shape(p, s, true);
   const bool fuse = p.ref_dim != 0;
   hipError_t e;
+  // Sparse launches (few samples per 8x8 value tile, e.g. decoder queries): a
+  // tile sort would cost more than it saves; grad_value is zero-filled and
+  // the sample pass adds each corner's contribution with float atomics.
+  p.scatter = (int64_t)p.Lq * p.LK < 32 * (int64_t)p.TPI ? 1 : 0;
   // 0. fused inputs: every sample's location and weight, formed once into
-  //    the workspace, are the loc and attn of the passes below
-  if (fuse) {
+  //    the workspace, are the loc and attn of the passes below (formed by
+  //    the counting pass itself on the dense route when a pair's L*K samples
+  //    fit one lane segment)
+  p.form_inputs = fuse && !p.scatter && (p.LK & (p.LK - 1)) == 0 && p.LK <= 64 ? 1 : 0;
+  if (fuse && !p.form_inputs) {
     Params q = p;
     q.seg_softmax = (p.LK & (p.LK - 1)) == 0 && p.LK <= 64 ? 1 : 0;
     const int64_t items = q.seg_softmax ? p.pairs * p.LK : p.pairs;
@@ -1557,10 +1587,10 @@ hipError_t launch_backward(const Params &p_in, DType dt, const LaunchShape &s, h
     p.loc = p.ws.floc;
     p.attn = p.ws.fattn;
   }
-  // Sparse launches (few samples per 8x8 value tile, e.g. decoder queries): a
-  // tile sort would cost more than it saves; grad_value is zero-filled and
-  // the sample pass adds each corner's contribution with float atomics.
-  p.scatter = (int64_t)p.Lq * p.LK < 32 * (int64_t)p.TPI ? 1 : 0;
+  if (fuse && p.form_inputs) {
+    p.loc = p.ws.floc;  // written by the counting pass, read by the passes after it
+    p.attn = p.ws.fattn;
+  }
   if (p.scatter) {
     if ((e = launch_zero(p.grad_value, (int64_t)p.N * p.S * p.M * p.D, stream)) != hipSuccess) return e;
     if ((e = launch_pairs(false, p, dt, s, stream)) != hipSuccess) return e;
