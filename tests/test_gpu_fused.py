@@ -92,6 +92,24 @@ def test_fused_backward_encoder_small_maps_full(K):
     _check_grads(w, got, ref, w.ref, w.offsets)
 
 
+@pytest.mark.parametrize("L,K,kind,ref_dim", [(4, 16, "encoder", 2), (2, 2, "encoder", 2), (1, 2, "encoder", 2),
+                                               (4, 4, "decoder", 4)])
+def test_fused_backward_dense_route_point_counts(L, K, kind, ref_dim):
+    """The tile-sorted route, where the counting pass forms each sample's
+    location and softmax weight itself (L*K a power of two up to 64: a pair's
+    logits in segments of 2 to 64 lanes, a whole wave at 64), for reference
+    points and for boxes (300 box queries on small maps)."""
+    shapes = SMALL_LEVELS[:L]
+    kw = dict(Lq=300) if kind == "decoder" else {}
+    w = fused_workload(kind, N=2, shapes=shapes, K=K, ref_dim=ref_dim, seed=45 + L + K, with_grad=True, **kw)
+    tiles = sum(((h + 7) // 8) * ((wd + 7) // 8) for h, wd in shapes)
+    assert w.dims["Lq"] * L * K >= 32 * tiles  # the dense route
+    note(f"fused backward dense route {kind} ref_dim={ref_dim} L={L} K={K}")
+    got = _gpu_fused_backward(w)
+    ref = msda_fused_backward(*_oracle_args(w), w.grad_out)
+    _check_grads(w, got, ref, w.ref, w.offsets)
+
+
 @pytest.mark.parametrize("ref_dim,dtype", [(2, "f32"), (4, "f32"), (4, "bf16")])
 def test_fused_backward_decoder_full_config(ref_dim, dtype):
     w = fused_workload("decoder", N=2, Lq=300, ref_dim=ref_dim, dtype=dtype, seed=50 + ref_dim, with_grad=True)
